@@ -1,0 +1,99 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by monkeypatching) and check that the
+pins in test_oracle_pins.py catch each of them. A pin set that lets a mutation through is too
+weak."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oatt
+import oracle.energy as oen
+import oracle.select as osel
+from tests import test_oracle_pins as pins
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _scores_unscaled(qbar, kbar, scale=None):
+    return np.matmul(np.asarray(qbar, np.float64), np.swapaxes(np.asarray(kbar, np.float64), -1, -2))
+
+
+def _scores_sqrt_wrong(qbar, kbar, scale=None):
+    d = qbar.shape[-1]
+    return np.matmul(np.asarray(qbar, np.float64), np.swapaxes(np.asarray(kbar, np.float64), -1, -2)) / d
+
+
+def _topk_ascending(scores, forced, k):
+    return osel._orig_select_topk(-np.asarray(scores, np.float64), forced, k)
+
+
+def _topk_ties_high(scores, forced, k):
+    s = np.asarray(scores, np.float64)
+    flipped = s[..., ::-1]
+    return osel._orig_select_topk(flipped, forced[::-1], k)[..., ::-1]
+
+
+def _budget_floor(density, n):
+    return min(n, int(math.floor(density * n)))
+
+
+def _mass_strict(p, forced, tau):
+    # "reaches" taken as strictly greater: bump the threshold by one unit
+    orig = osel.mass_threshold_units
+    try:
+        osel.mass_threshold_units = lambda t: orig(t) + 1
+        return osel._orig_select_mass(p, forced, tau)
+    finally:
+        osel.mass_threshold_units = orig
+
+
+def _mass_ignore_forced(p, forced, tau):
+    kept = osel._orig_select_mass(np.where(forced, 0.0, np.asarray(p, np.float64)), forced, tau)
+    return kept
+
+
+def _energy_no_divisor(q, k, rows, scale=None, block=oracle.BLOCK):
+    return oen._orig_block_energy_rows(q, k, rows, scale, block) * block
+
+
+def _softmax_weighted_unnormalised(logits, values):
+    m = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    return e @ values, (m + np.log(e.sum(axis=-1, keepdims=True)))[..., 0]
+
+
+MUTATIONS = {
+    "scores without 1/sqrt(d)": (osel, "block_scores", _scores_unscaled,
+                                 [pins.test_scores_closed_form_asymmetric, pins.test_mean_field_identity]),
+    "scores scaled by 1/d": (osel, "block_scores", _scores_sqrt_wrong,
+                             [pins.test_scores_closed_form_asymmetric]),
+    "Top-K ascending": (osel, "select_topk", _topk_ascending, [pins.test_topk_golden]),
+    "Top-K ties to the higher index": (osel, "select_topk", _topk_ties_high, [pins.test_topk_golden]),
+    "budget rounded down": (osel, "topk_budget", _budget_floor, [pins.test_topk_golden]),
+    "mass uses strict >": (osel, "select_mass", _mass_strict, [pins.test_mass_golden]),
+    "mass ignores forced blocks": (osel, "select_mass", _mass_ignore_forced, [pins.test_mass_golden]),
+    "energy without 1/B": (oen, "block_energy_rows", _energy_no_divisor,
+                           [pins.test_energy_rows_sum_to_one]),
+    "attention without normalisation": (oatt, "_softmax_weighted", _softmax_weighted_unnormalised,
+                                        [pins.test_density_one_equals_dense_toy]),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    module, attr, fn, tests = MUTATIONS[name]
+    orig = getattr(module, attr)
+    monkeypatch.setattr(module, "_orig_" + attr, orig, raising=False)
+    monkeypatch.setattr(module, attr, fn)
+    # the package re-exports the names; patch those too so pins that call oracle.X see it
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    caught = [t.__name__ for t in tests if _fails(t)]
+    assert caught, f"no pin caught the mutation: {name}"

@@ -1,0 +1,411 @@
+"""Pins of the oracle against facts fixed outside it: hand-worked examples, closed forms,
+invariants of the definitions, brute force on tiny inputs and independent library routines.
+
+Each test names what a plausible mistake in the oracle would break.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from synth import BLOCK, WORKLOADS, make_qkv, small_variants
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- partition and pooling
+
+def test_partition_whole_blocks_only():
+    assert oracle.n_blocks(1024) == 8
+    assert oracle.n_blocks(144896) == 1132
+    for bad in (0, 127, 1000, -128):
+        with pytest.raises(ValueError):
+            oracle.n_blocks(bad)
+
+
+def test_pool_closed_form():
+    # x[t, j] = t + 1000 j: the mean over block i is 128 i + 63.5 + 1000 j.
+    # Pins the block size, the pooled axis and the divisor.
+    L, d = 4 * BLOCK, 3
+    t = np.arange(L, dtype=np.float64)[:, None]
+    j = np.arange(d, dtype=np.float64)[None, :]
+    x = (t + 1000.0 * j)[None, None]
+    got = oracle.pool(x)
+    want = (128.0 * np.arange(4)[:, None] + 63.5 + 1000.0 * j)[None, None]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_pool_keeps_heads_apart():
+    x = np.zeros((1, 2, BLOCK, 2))
+    x[0, 0] = 1.0
+    x[0, 1] = -3.0
+    got = oracle.pool(x)
+    np.testing.assert_array_equal(got[0, 0, 0], [1.0, 1.0])
+    np.testing.assert_array_equal(got[0, 1, 0], [-3.0, -3.0])
+
+
+# ---------------------------------------------------------------- block scores
+
+def test_scores_closed_form_asymmetric():
+    # Query block i holds (i+1) e_i in every token; key block c holds a_c with a_c[j] = (c+1)(j+1).
+    # Then S_ic = (i+1) * a_c[i] / sqrt(d) = (i+1)^2 (c+1) / sqrt(d): not symmetric in (i, c),
+    # so a transposed product or a missing / wrong scale fails.
+    d, nqb, nkb = 4, 3, 5
+    q = np.zeros((1, 1, nqb * BLOCK, d))
+    for i in range(nqb):
+        q[0, 0, i * BLOCK:(i + 1) * BLOCK, i] = i + 1
+    k = np.zeros((1, 1, nkb * BLOCK, d))
+    for c in range(nkb):
+        k[0, 0, c * BLOCK:(c + 1) * BLOCK, :] = (c + 1) * (np.arange(d) + 1)
+    s = oracle.block_scores(oracle.pool(q), oracle.pool(k))[0, 0]
+    want = np.array([[(i + 1) ** 2 * (c + 1) / math.sqrt(d) for c in range(nkb)] for i in range(nqb)])
+    np.testing.assert_allclose(s, want, rtol=1e-15, atol=0)
+
+
+def test_scores_equal_mean_token_logit():
+    # Bilinearity: the score of two pooled blocks is the mean of the 128 x 128 token logits
+    # q_t . k_s / sqrt(d). Computed here by brute force over token pairs.
+    rng = np.random.default_rng(1)
+    d = 8
+    q = rng.standard_normal((1, 1, 2 * BLOCK, d))
+    k = rng.standard_normal((1, 1, 3 * BLOCK, d))
+    s = oracle.block_scores(oracle.pool(q), oracle.pool(k))[0, 0]
+    for i in range(2):
+        for c in range(3):
+            qi = q[0, 0, i * BLOCK:(i + 1) * BLOCK]
+            kc = k[0, 0, c * BLOCK:(c + 1) * BLOCK]
+            total = 0.0
+            for a in range(BLOCK):
+                total += float(np.sum(kc @ qi[a]))
+            assert s[i, c] == pytest.approx(total / (BLOCK * BLOCK) / math.sqrt(d), rel=1e-12, abs=1e-13)
+
+
+# ---------------------------------------------------------------- forced set
+
+def test_forced_ranges():
+    m = oracle.forced_blocks(10, (0, 2), (4, 7))
+    assert np.flatnonzero(m).tolist() == [0, 1, 4, 5, 6]
+    assert not oracle.forced_blocks(5, (0, 0), (0, 0)).any()
+    with pytest.raises(ValueError):
+        oracle.forced_blocks(5, (0, 3), (2, 4))      # overlap
+    with pytest.raises(ValueError):
+        oracle.forced_blocks(5, (0, 6), (0, 0))      # outside
+    with pytest.raises(ValueError):
+        oracle.forced_blocks(5, (3, 2), (0, 0))      # reversed
+
+
+# ---------------------------------------------------------------- Top-K
+
+def test_topk_golden():
+    g = _load("topk_rows.json")
+    for case in g["cases"]:
+        s = np.array(case["scores"])
+        forced = oracle.forced_blocks(s.size, tuple(case["text"]), tuple(case["extra"]))
+        k = oracle.topk_budget(case["density"], int((~forced).sum()))
+        assert k == case["k"], case["name"]
+        kept = oracle.select_topk(s[None], forced, k)[0]
+        assert np.flatnonzero(kept).tolist() == case["kept"], case["name"]
+    for b in g["budgets"]:
+        assert oracle.topk_budget(b["density"], b["candidates"]) == b["k"], b["note"]
+
+
+def _brute_topk(row, forced, k):
+    cand = [c for c in range(len(row)) if not forced[c]]
+    # Python compares -0.0 == 0.0, so signed zeros tie and fall back to the index
+    order = sorted(cand, key=lambda c: (-row[c], c))
+    return sorted(set(np.flatnonzero(forced).tolist()) | set(order[:k]))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    nkb = int(rng.integers(2, 40))
+    rows = rng.integers(-3, 4, size=(25, nkb)).astype(np.float64)   # many ties
+    rows[rng.random(rows.shape) < 0.1] = -0.0
+    t0 = int(rng.integers(0, nkb))
+    forced = oracle.forced_blocks(nkb, (0, t0 // 2), (t0 // 2, t0 // 2 + (t0 % 3 > 0)))
+    ncand = int((~forced).sum())
+    for k in sorted({0, 1, ncand // 2, ncand}):
+        kept = oracle.select_topk(rows, forced, k)
+        for r in range(rows.shape[0]):
+            assert np.flatnonzero(kept[r]).tolist() == _brute_topk(rows[r].tolist(), forced, k)
+
+
+def test_topk_all_equal_row_keeps_lowest_indices():
+    forced = oracle.forced_blocks(9, (0, 2), (0, 0))
+    kept = oracle.select_topk(np.full((1, 9), 0.25), forced, 3)[0]
+    assert np.flatnonzero(kept).tolist() == [0, 1, 2, 3, 4]
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10_000), st.floats(0.01, 100.0), st.floats(-50.0, 50.0))
+def test_topk_invariant_to_scale_and_shift(seed, a, b):
+    # Positive scaling and a per-row shift do not change the order, hence not the mask.
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((4, 23))
+    forced = oracle.forced_blocks(23, (0, 3), (0, 0))
+    base = oracle.select_topk(s, forced, 6)
+    # only compare when the transformed scores keep distinct values distinct in float64
+    t = s * a + b
+    if len(np.unique(t)) == len(np.unique(s)):
+        np.testing.assert_array_equal(oracle.select_topk(t, forced, 6), base)
+
+
+def test_topk_is_an_order_statistic():
+    # Every kept candidate scores at least as high as every dropped candidate.
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal((50, 31))
+    forced = oracle.forced_blocks(31, (0, 4), (10, 12))
+    kept = oracle.select_topk(s, forced, 9)
+    for r in range(50):
+        kc = s[r][kept[r] & ~forced]
+        dc = s[r][~kept[r] & ~forced]
+        assert kc.size == 9 and kc.min() >= dc.max()
+
+
+# ---------------------------------------------------------------- mass threshold
+
+def test_mass_golden():
+    g = _load("mass_rows.json")
+    for case in g["cases"]:
+        p = np.array(case["p"])
+        forced = np.zeros(p.size, bool)
+        forced[case["forced"]] = True
+        kept = oracle.select_mass(p[None], forced, case["tau"])[0]
+        assert np.flatnonzero(kept).tolist() == case["kept"], case["name"]
+
+
+def test_mass_units_exact():
+    assert int(oracle.mass_units(np.array([0.5]))[0]) == 2 ** 61
+    assert int(oracle.mass_units(np.array([2.0 ** -62]))[0]) == 1
+    assert int(oracle.mass_units(np.array([2.0 ** -63]))[0]) == 0
+    assert oracle.mass_threshold_units(0.75) == 3 * 2 ** 60
+    assert oracle.mass_threshold_units(0.9) == math.ceil(0.9 * 2.0 ** 62)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mass_is_minimal_prefix_by_enumeration(seed):
+    # Brute force over every subset containing the forced blocks: the kept set has the minimum
+    # size among sets whose fixed-point mass reaches the threshold, and it is a prefix of the
+    # (energy desc, index asc) order. Catches a wrong sort direction, a strict '>' and
+    # forgetting the forced mass.
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(3, 11))
+    p = rng.dirichlet(np.full(n, 0.4))
+    p[rng.random(n) < 0.2] = p[0]                          # some exact ties
+    p = p / p.sum()
+    forced = np.zeros(n, bool)
+    if seed % 2:
+        forced[: int(rng.integers(1, 3))] = True
+    tau = float(rng.uniform(0.3, 0.95))
+    kept = oracle.select_mass(p[None], forced, tau)[0]
+    u = [int(x) for x in oracle.mass_units(p)]
+    theta = oracle.mass_threshold_units(tau)
+    cand = [c for c in range(n) if not forced[c]]
+    fset = [c for c in range(n) if forced[c]]
+    best = None
+    for size in range(0, len(cand) + 1):
+        for sub in itertools.combinations(cand, size):
+            if sum(u[c] for c in fset) + sum(u[c] for c in sub) >= theta:
+                best = size
+                break
+        if best is not None:
+            break
+    if best is None:
+        assert kept.all()
+        return
+    assert int(kept.sum()) - len(fset) == best
+    order = sorted(cand, key=lambda c: (-p[c], c))
+    assert sorted(np.flatnonzero(kept & ~forced).tolist()) == sorted(order[:best])
+
+
+def test_mass_shift_invariant():
+    # Softmax is invariant to a per-row shift of the scores, so the mass mask is too.
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((6, 17)) * 3
+    forced = np.zeros(17, bool)
+    a = oracle.select_mass(oracle.block_softmax(s), forced, 0.9)
+    b = oracle.select_mass(oracle.block_softmax(s + 11.0), forced, 0.9)
+    np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- block energy, Eq. (5)
+
+def test_energy_rows_sum_to_one():
+    w = small_variants()["star_mid_small"]
+    q, k, _ = (t.double().numpy() for t in make_qkv(w.with_(heads=1), seed=5))
+    e = oracle.block_energy_rows(q, k, rows=range(w.n_q_blocks))
+    np.testing.assert_allclose(e.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert (e >= 0).all()
+
+
+def test_mean_field_identity():
+    # With every token of a block equal to the block's vector, P_ij = exp(S_rc) / (B sum_c'
+    # exp(S_rc')) inside block pair (r, c), so Eq. (5) gives E_rc = softmax_c(S_rc) exactly:
+    # the pooled-score softmax with scale 1/sqrt(d) is the token-level energy. The two mass
+    # masks then agree. Pins the score scale and the energy normalisation together.
+    rng = np.random.default_rng(11)
+    d, nqb, nkb = 16, 3, 9
+    qc = rng.standard_normal((nqb, d)) * 1.5
+    kc = rng.standard_normal((nkb, d)) * 1.5
+    q = np.repeat(qc, BLOCK, axis=0)[None, None]
+    k = np.repeat(kc, BLOCK, axis=0)[None, None]
+    e_tok = oracle.block_energy_rows(q, k, rows=range(nqb))
+    p = oracle.block_softmax(oracle.block_scores(oracle.pool(q), oracle.pool(k)))[0, 0]
+    np.testing.assert_allclose(p, e_tok, rtol=1e-12, atol=1e-15)
+    forced = np.zeros(nkb, bool)
+    for tau in (0.5, 0.8, 0.95):
+        np.testing.assert_array_equal(oracle.select_mass(p, forced, tau),
+                                      oracle.select_mass(e_tok, forced, tau))
+
+
+# ---------------------------------------------------------------- attention
+
+def _torch_sdpa(q, k, v, kept):
+    tq, tk, tv = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (q, k, v))
+    if kept is None:
+        return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+    mask = torch.from_numpy(np.repeat(np.repeat(kept, BLOCK, axis=-2), BLOCK, axis=-1))
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask).numpy()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_three_ways(seed):
+    # The gather formulation, the -inf masked formulation and torch's SDPA (float64, boolean
+    # mask) agree on random masks.
+    rng = np.random.default_rng(seed)
+    bsz, h, nqb, nkb, d = 1, 2, 2, 4, 8
+    q = rng.standard_normal((bsz, h, nqb * BLOCK, d))
+    k = rng.standard_normal((bsz, h, nkb * BLOCK, d))
+    v = rng.standard_normal((bsz, h, nkb * BLOCK, d))
+    kept = rng.random((bsz, h, nqb, nkb)) < 0.5
+    kept[..., 0] = True                                  # no empty row for SDPA
+    row_ptr, col_idx = oracle.to_csr(kept.reshape(-1, nkb))
+    o1, l1 = oracle.attention_rows(q, k, v, row_ptr, col_idx)
+    o2, l2 = oracle.attention_masked(q, k, v, kept)
+    o3 = _torch_sdpa(q, k, v, kept)
+    o1 = o1.reshape(bsz, h, nqb * BLOCK, d)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o1, o3, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(l1.reshape(bsz, h, -1), l2, rtol=1e-12, atol=1e-12)
+    # lse against a direct log-sum-exp over the kept keys of one query
+    qi = q[0, 1, 5]
+    cols = np.flatnonzero(kept[0, 1, 0])
+    keys = np.concatenate([k[0, 1, c * BLOCK:(c + 1) * BLOCK] for c in cols])
+    direct = math.log(sum(math.exp(float(x)) for x in keys @ qi / math.sqrt(d)))
+    assert l1.reshape(bsz, h, -1)[0, 1, 5] == pytest.approx(direct, rel=1e-12)
+
+
+def test_empty_row_gives_zero_output():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, 1, BLOCK, 4))
+    k = rng.standard_normal((1, 1, 2 * BLOCK, 4))
+    kept = np.zeros((1, 1, 1, 2), bool)
+    row_ptr, col_idx = oracle.to_csr(kept.reshape(-1, 2))
+    o, lse = oracle.attention_rows(q, k, k, row_ptr, col_idx)
+    assert (o == 0).all() and np.isneginf(lse).all()
+    o2, lse2 = oracle.attention_masked(q, k, k, kept)
+    assert (o2 == 0).all() and np.isneginf(lse2).all()
+
+
+def test_attention_closed_form_identical_keys():
+    # All kept keys identical: uniform weights, O = mean of the kept values, and
+    # lse = log(#kept tokens) + q . k / sqrt(d).
+    rng = np.random.default_rng(4)
+    d = 6
+    q = rng.standard_normal((1, 1, BLOCK, d))
+    kvec = rng.standard_normal(d)
+    k = np.tile(kvec, (1, 1, 3 * BLOCK, 1))
+    v = rng.standard_normal((1, 1, 3 * BLOCK, d))
+    kept = np.array([True, False, True])
+    row_ptr, col_idx = oracle.to_csr(kept[None])
+    o, lse = oracle.attention_rows(q, k, v, row_ptr, col_idx)
+    vmean = np.concatenate([v[0, 0, :BLOCK], v[0, 0, 2 * BLOCK:]]).mean(axis=0)
+    np.testing.assert_allclose(o[0], np.tile(vmean, (BLOCK, 1)), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[0], math.log(2 * BLOCK) + q[0, 0] @ kvec / math.sqrt(d),
+                               rtol=1e-12)
+
+
+def test_density_one_equals_dense_toy():
+    # Toy workload at density 1.0: every block is kept and the sparse result equals dense
+    # attention (the oracle's own dense path and torch SDPA).
+    w = WORKLOADS["toy_dense"]
+    q, k, v = (t.double().numpy() for t in make_qkv(w, seed=0))
+    sel = oracle.sparse_select(q, k, w.text, w.extra, w.mode, w.param)
+    assert sel["kept"].all()
+    o, lse = oracle.attention_rows(q, k, v, sel["row_ptr"], sel["col_idx"])
+    od, lsed = oracle.attention_dense(q, k, v)
+    np.testing.assert_allclose(o.reshape(od.shape), od, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(o.reshape(od.shape), _torch_sdpa(q, k, v, None), rtol=1e-10, atol=1e-12)
+
+
+def test_within_block_permutation():
+    # Permuting tokens inside blocks leaves pooled vectors and masks unchanged, and permutes
+    # the output rows the same way.
+    w = small_variants()["star_mid_small"].with_(heads=1)
+    q, k, v = (t.double().numpy() for t in make_qkv(w, seed=2))
+    rng = np.random.default_rng(0)
+    pq = np.concatenate([b * BLOCK + rng.permutation(BLOCK) for b in range(w.n_q_blocks)])
+    pk = np.concatenate([b * BLOCK + rng.permutation(BLOCK) for b in range(w.n_k_blocks)])
+    a = oracle.sparse_select(q, k, w.text, w.extra, "topk", w.param)
+    b = oracle.sparse_select(q[:, :, pq], k[:, :, pk], w.text, w.extra, "topk", w.param)
+    np.testing.assert_allclose(a["qbar"], b["qbar"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(a["kept"], b["kept"])
+    oa, _ = oracle.attention_rows(q, k, v, a["row_ptr"], a["col_idx"])
+    ob, _ = oracle.attention_rows(q[:, :, pq], k[:, :, pk], v[:, :, pk], b["row_ptr"], b["col_idx"])
+    np.testing.assert_allclose(oa.reshape(-1, w.head_dim)[pq], ob.reshape(-1, w.head_dim), rtol=1e-10,
+                               atol=1e-12)
+
+
+# ---------------------------------------------------------------- CSR and the whole selection
+
+@pytest.mark.parametrize("name", list(small_variants()))
+def test_select_structure_small_workloads(name):
+    w = small_variants()[name]
+    q, k, _ = (t.double().numpy() for t in make_qkv(w, seed=1))
+    sel = oracle.sparse_select(q, k, w.text, w.extra, w.mode, w.param)
+    rp, ci = sel["row_ptr"], sel["col_idx"]
+    forced = np.flatnonzero(sel["forced"])
+    ncand = w.n_k_blocks - forced.size
+    assert rp[0] == 0 and rp.size == w.rows + 1 and ci.size == rp[-1]
+    for r in range(w.rows):
+        cols = ci[rp[r]:rp[r + 1]]
+        assert (np.diff(cols) > 0).all()
+        assert set(forced.tolist()) <= set(cols.tolist())
+        if w.mode == "topk":
+            assert cols.size == forced.size + oracle.topk_budget(w.param, ncand)
+    if w.mode == "mass":
+        p = sel["scores"].reshape(-1, w.n_k_blocks)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+        kept = sel["kept"].reshape(-1, w.n_k_blocks)
+        assert (np.where(kept, p, 0).sum(axis=1) >= w.param - 1e-12).all()
+
+
+def test_csr_closed_form():
+    kept = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 1]], bool)
+    rp, ci = oracle.to_csr(kept)
+    assert rp.tolist() == [0, 2, 2, 5]
+    assert ci.tolist() == [0, 2, 0, 1, 2]
+
+
+# ---------------------------------------------------------------- cross-input vote
+
+def test_vote_worked_example():
+    g = _load("vote_example.json")
+    n = g["n_inputs"]
+    counts = g["counts"]
+    masks = np.zeros((n, len(counts)), bool)
+    for j, c in enumerate(counts):
+        masks[:c, j] = True
+    assert oracle.vote_masks(masks, g["rho"]).tolist() == g["kept"]
