@@ -1,0 +1,211 @@
+"""Per-head dynamic block-sparse attention for MI355X (gfx950).
+
+Python binding over the C ABI of libdbsp.so (include/dbsp.h). Only argument marshalling
+happens here: torch tensors supply device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.
+
+    import dynamic_block_sparse_pool_amd as dbsp
+    idx = dbsp.sparse_select(q, k, text_blocks=(0, 4), density=0.09375)
+    o = dbsp.sparse_attn_fwd(q, k, v, idx)
+
+q is [batch, heads, Lq, d] and k, v are [batch, heads, Lk, d], contiguous CUDA tensors
+(bfloat16 with d = 128, or float32 with d = 64 / 128), Lq and Lk multiples of 128.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional, Tuple
+
+import torch
+
+from . import _abi
+from ._abi import DBSP_BLOCK, DbspError
+
+__all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "topk_budget", "select_nnz_bound",
+           "select_workspace_bytes", "DbspError", "DBSP_BLOCK", "version"]
+
+
+@dataclasses.dataclass
+class BlockIndex:
+    """Forward-only CSR skip list: row r = (b * heads + h) * n_q_blocks + i lists the key blocks
+    query block i of head h attends to, ascending. nnz lives in row_ptr[-1] on the device."""
+    row_ptr: torch.Tensor          # int32 [rows + 1]
+    col_idx: torch.Tensor          # int32 [capacity]
+    n_q_blocks: int
+    n_k_blocks: int
+    scores: Optional[torch.Tensor] = None   # float32 [rows, n_k_blocks] if requested
+
+    @property
+    def rows(self) -> int:
+        return self.row_ptr.numel() - 1
+
+    def nnz(self) -> int:
+        """Number of kept (row, key block) pairs; synchronises with the device."""
+        return int(self.row_ptr[-1].item())
+
+
+def version() -> int:
+    return int(_abi.load().dbsp_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _abi.DBSP_BF16
+    if t.dtype == torch.float32:
+        return _abi.DBSP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor) -> _abi.Dims:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, L, head_dim]")
+    if q.shape[0] != k.shape[0] or q.shape[1] != k.shape[1] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} vs k {tuple(k.shape)}")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    return _abi.Dims(q.shape[0], q.shape[1], q.shape[2], k.shape[2], q.shape[3], _dtype_code(q))
+
+
+def _range(r) -> _abi.Range:
+    if r is None:
+        return _abi.Range(0, 0)
+    b, e = r
+    return _abi.Range(int(b), int(e))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_device_tensor(name: str, t: torch.Tensor) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def topk_budget(n_k_blocks: int, density: float, text_blocks=(0, 0), dense_extra_blocks=(0, 0),
+                topk_override: int = -1) -> int:
+    """K, the number of non-forced key blocks Top-K keeps per row (host-only query)."""
+    dims = _abi.Dims(1, 1, DBSP_BLOCK, int(n_k_blocks) * DBSP_BLOCK, 128, _abi.DBSP_BF16)
+    out = ctypes.c_int32()
+    _abi.check(_abi.load().dbsp_topk_budget(ctypes.byref(dims), float(density), _range(text_blocks),
+                                            _range(dense_extra_blocks), int(topk_override),
+                                            ctypes.byref(out)), "dbsp_topk_budget")
+    return out.value
+
+
+def select_nnz_bound(dims: _abi.Dims, mode: int, param: float, text_blocks, extra_blocks,
+                     topk_override: int = -1) -> int:
+    out = ctypes.c_int64()
+    _abi.check(_abi.load().dbsp_select_nnz_bound(ctypes.byref(dims), int(mode), float(param),
+                                                 _range(text_blocks), _range(extra_blocks),
+                                                 int(topk_override), ctypes.byref(out)),
+               "dbsp_select_nnz_bound")
+    return out.value
+
+
+def select_workspace_bytes(dims: _abi.Dims, mode: int) -> int:
+    out = ctypes.c_uint64()
+    _abi.check(_abi.load().dbsp_select_workspace_bytes(ctypes.byref(dims), int(mode),
+                                                       ctypes.byref(out)),
+               "dbsp_select_workspace_bytes")
+    return out.value
+
+
+class SelectPlan:
+    """Buffers for repeated dbsp_sparse_select calls of one shape (CSR, workspace, scores).
+    Allocating them once keeps the hot loop free of allocations."""
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, text_blocks=(0, 0),
+                 dense_extra_blocks=(0, 0), density: Optional[float] = None,
+                 mass: Optional[float] = None, topk_override: int = -1,
+                 score_scale: float = 0.0, return_scores: bool = False):
+        if (density is None) == (mass is None):
+            raise ValueError("give exactly one of density (Top-K) or mass (cumulative mass)")
+        _check_device_tensor("q", q)
+        _check_device_tensor("k", k)
+        self.dims = _dims(q, k)
+        self.mode = _abi.DBSP_TOPK if density is not None else _abi.DBSP_MASS
+        self.param = float(density if density is not None else mass)
+        self.text = _range(text_blocks)
+        self.extra = _range(dense_extra_blocks)
+        self.topk_override = int(topk_override)
+        self.score_scale = float(score_scale)
+        self.device = q.device
+        rows = self.dims.batch * self.dims.heads * (self.dims.lq // DBSP_BLOCK)
+        nkb = self.dims.lk // DBSP_BLOCK
+        self.capacity = select_nnz_bound(self.dims, self.mode, self.param, text_blocks,
+                                         dense_extra_blocks, self.topk_override)
+        ws = select_workspace_bytes(self.dims, self.mode)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+        self.col_idx = torch.empty(max(self.capacity, 1), dtype=torch.int32, device=q.device)
+        self.scores = (torch.empty((rows, nkb), dtype=torch.float32, device=q.device)
+                       if return_scores else None)
+        self.index = BlockIndex(self.row_ptr, self.col_idx, self.dims.lq // DBSP_BLOCK, nkb,
+                                self.scores)
+
+    def run(self, q: torch.Tensor, k: torch.Tensor) -> BlockIndex:
+        d = _dims(q, k)
+        if (d.batch, d.heads, d.lq, d.lk, d.head_dim, d.dtype) != (
+                self.dims.batch, self.dims.heads, self.dims.lq, self.dims.lk, self.dims.head_dim,
+                self.dims.dtype):
+            raise ValueError("q / k shape or dtype differs from the plan")
+        _check_device_tensor("q", q)
+        _check_device_tensor("k", k)
+        st = _abi.load().dbsp_sparse_select(
+            _ptr(q), _ptr(k), ctypes.byref(self.dims), self.text, self.extra, self.mode,
+            self.param, self.topk_override, self.score_scale, _ptr(self.row_ptr),
+            _ptr(self.col_idx), self.col_idx.numel(), _ptr(self.scores), _ptr(self.workspace),
+            self.workspace.numel(), _stream(q.device))
+        _abi.check(st, "dbsp_sparse_select")
+        return self.index
+
+
+def sparse_select(q: torch.Tensor, k: torch.Tensor, text_blocks: Tuple[int, int] = (0, 0),
+                  dense_extra_blocks: Tuple[int, int] = (0, 0), density: Optional[float] = None,
+                  mass: Optional[float] = None, topk_override: int = -1, score_scale: float = 0.0,
+                  return_scores: bool = False) -> BlockIndex:
+    """Pool Q and K per 128-token block, score block pairs per head, keep the forced ranges and
+    pick the remaining key blocks per (head, query block): Top-K at `density`, or the shortest
+    cumulative-mass prefix reaching `mass`. Returns the CSR skip list."""
+    plan = SelectPlan(q, k, text_blocks, dense_extra_blocks, density, mass, topk_override,
+                      score_scale, return_scores)
+    return plan.run(q, k)
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: BlockIndex,
+                    softmax_scale: float = 0.0, out_dtype: Optional[torch.dtype] = None,
+                    return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None):
+    """Forward attention of every query block over the tokens of its kept key blocks only.
+    Returns O (and lse if return_lse)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t)
+    dims = _dims(q, k)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    rows = dims.batch * dims.heads * (dims.lq // DBSP_BLOCK)
+    if index.row_ptr.numel() != rows + 1:
+        raise ValueError("index was built for a different shape")
+    if index.row_ptr.dtype != torch.int32 or index.col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    odt = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
+    if out is None:
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if return_lse and lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    st = _abi.load().dbsp_sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), _ptr(index.row_ptr), _ptr(index.col_idx),
+        index.col_idx.numel(), float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
+        _stream(q.device))
+    _abi.check(st, "dbsp_sparse_attn_fwd")
+    return (out, lse) if return_lse else out

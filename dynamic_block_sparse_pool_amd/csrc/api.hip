@@ -1,0 +1,253 @@
+// Host side of the C ABI declared in include/dbsp.h: argument validation (pure host code, runs
+// before any HIP call), workspace and nnz sizing, and kernel launches.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/dbsp.h"
+#include "common.hpp"
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+bool shape_ok(const dbsp_dims* d) {
+  if (!d) return false;
+  if (d->batch <= 0 || d->heads <= 0 || d->lq <= 0 || d->lk <= 0) return false;
+  if (d->lq % DBSP_BLOCK || d->lk % DBSP_BLOCK) return false;
+  if (d->dtype != DBSP_F32 && d->dtype != DBSP_BF16) return false;
+  if (d->head_dim <= 0) return false;
+  return true;
+}
+
+bool dtype_supported(const dbsp_dims* d) {
+  if (d->dtype == DBSP_BF16) return d->head_dim == 128 || d->head_dim == 64;
+  return d->head_dim == 64 || d->head_dim == 128;
+}
+
+bool attn_supported(const dbsp_dims* d) {
+  if (d->dtype == DBSP_BF16) return d->head_dim == 128;
+  return d->head_dim == 64 || d->head_dim == 128;
+}
+
+int64_t rows_of(const dbsp_dims* d) {
+  return (int64_t)d->batch * d->heads * (d->lq / DBSP_BLOCK);
+}
+
+// Validates the two forced ranges against nkb; returns the forced count or -1.
+int32_t forced_count(int32_t nkb, dbsp_range t, dbsp_range e) {
+  const dbsp_range r[2] = {t, e};
+  for (int i = 0; i < 2; ++i)
+    if (r[i].begin < 0 || r[i].begin > r[i].end || r[i].end > nkb) return -1;
+  const bool both = t.begin < t.end && e.begin < e.end;
+  if (both && t.begin < e.end && e.begin < t.end) return -1;  // overlap
+  return (t.end - t.begin) + (e.end - e.begin);
+}
+
+int32_t topk_k(const dbsp_dims* d, double density, dbsp_range t, dbsp_range e, int32_t override_k,
+               int32_t* k_out, int32_t* forced_out) {
+  if (!shape_ok(d) || !k_out) return DBSP_ERR_INVALID_ARG;
+  const int32_t nkb = d->lk / DBSP_BLOCK;
+  const int32_t f = forced_count(nkb, t, e);
+  if (f < 0) return DBSP_ERR_INVALID_ARG;
+  const int32_t ncand = nkb - f;
+  int64_t k;
+  if (override_k >= 0) {
+    if (override_k > ncand) return DBSP_ERR_INVALID_ARG;
+    k = override_k;
+  } else {
+    if (!(density >= 0.0 && density <= 1.0)) return DBSP_ERR_INVALID_ARG;  // also rejects NaN
+    k = (int64_t)ceil(density * (double)ncand);
+    if (k > ncand) k = ncand;
+  }
+  *k_out = (int32_t)k;
+  if (forced_out) *forced_out = f;
+  return DBSP_OK;
+}
+
+int32_t nnz_bound(const dbsp_dims* d, int32_t mode, double param, dbsp_range t, dbsp_range e,
+                  int32_t override_k, int64_t* out) {
+  if (!shape_ok(d) || !out) return DBSP_ERR_INVALID_ARG;
+  const int32_t nkb = d->lk / DBSP_BLOCK;
+  if (mode == DBSP_TOPK) {
+    int32_t k, f;
+    int32_t st = topk_k(d, param, t, e, override_k, &k, &f);
+    if (st != DBSP_OK) return st;
+    *out = rows_of(d) * (int64_t)(f + k);
+    return DBSP_OK;
+  }
+  if (mode == DBSP_MASS) {
+    if (forced_count(nkb, t, e) < 0) return DBSP_ERR_INVALID_ARG;
+    if (!(param > 0.0 && param <= 1.0)) return DBSP_ERR_INVALID_ARG;
+    *out = rows_of(d) * (int64_t)nkb;
+    return DBSP_OK;
+  }
+  return DBSP_ERR_INVALID_ARG;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
+
+struct WorkspaceLayout {
+  uint64_t qbar, kbar, counts, masks, total;
+};
+
+WorkspaceLayout layout_of(const dbsp_dims* d, int32_t mode) {
+  WorkspaceLayout w{};
+  const uint64_t bh = (uint64_t)d->batch * d->heads;
+  const uint64_t nqb = d->lq / DBSP_BLOCK, nkb = d->lk / DBSP_BLOCK;
+  uint64_t off = 0;
+  w.qbar = off;
+  off = align256(off + bh * nqb * d->head_dim * sizeof(float));
+  w.kbar = off;
+  off = align256(off + bh * nkb * d->head_dim * sizeof(float));
+  if (mode == DBSP_MASS) {
+    w.counts = off;
+    off = align256(off + bh * nqb * sizeof(int32_t));
+    w.masks = off;
+    off = align256(off + bh * nqb * ((nkb + 63) / 64) * sizeof(uint64_t));
+  }
+  w.total = off;
+  return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dbsp_version(void) { return kVersion; }
+
+const char* dbsp_status_string(int32_t status) {
+  switch (status) {
+    case DBSP_OK: return "ok";
+    case DBSP_ERR_INVALID_ARG: return "invalid argument";
+    case DBSP_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case DBSP_ERR_CAPACITY: return "col_idx capacity below the nnz bound";
+    case DBSP_ERR_WORKSPACE: return "workspace missing or too small";
+    case DBSP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t dbsp_topk_budget(const dbsp_dims* dims, double density, dbsp_range text_blocks,
+                         dbsp_range dense_extra_blocks, int32_t topk_override, int32_t* k_out) {
+  return topk_k(dims, density, text_blocks, dense_extra_blocks, topk_override, k_out, nullptr);
+}
+
+int32_t dbsp_select_nnz_bound(const dbsp_dims* dims, int32_t mode, double density_or_mass,
+                              dbsp_range text_blocks, dbsp_range dense_extra_blocks,
+                              int32_t topk_override, int64_t* nnz_bound_out) {
+  return nnz_bound(dims, mode, density_or_mass, text_blocks, dense_extra_blocks, topk_override,
+                   nnz_bound_out);
+}
+
+int32_t dbsp_select_workspace_bytes(const dbsp_dims* dims, int32_t mode, uint64_t* bytes) {
+  if (!shape_ok(dims) || !bytes || (mode != DBSP_TOPK && mode != DBSP_MASS))
+    return DBSP_ERR_INVALID_ARG;
+  *bytes = layout_of(dims, mode).total;
+  return DBSP_OK;
+}
+
+int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
+                           dbsp_range text_blocks, dbsp_range dense_extra_blocks, int32_t mode,
+                           double density_or_mass, int32_t topk_override, float score_scale,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                           float* scores_out, void* workspace, uint64_t workspace_bytes,
+                           void* stream) {
+  if (!shape_ok(dims) || !q || !k || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
+  if (mode != DBSP_TOPK && mode != DBSP_MASS) return DBSP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return DBSP_ERR_INVALID_ARG;
+  if (!(isfinite(score_scale))) return DBSP_ERR_INVALID_ARG;
+  if (!dtype_supported(dims)) return DBSP_ERR_UNSUPPORTED;
+  const int32_t nkb = dims->lk / DBSP_BLOCK;
+  const int32_t nqb = dims->lq / DBSP_BLOCK;
+  if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  int64_t bound;
+  int32_t st = nnz_bound(dims, mode, density_or_mass, text_blocks, dense_extra_blocks,
+                         topk_override, &bound);
+  if (st != DBSP_OK) return st;
+  if (bound > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  if (col_capacity < bound) return DBSP_ERR_CAPACITY;
+  const WorkspaceLayout wl = layout_of(dims, mode);
+  if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255u))
+    return DBSP_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t bh = (int64_t)dims->batch * dims->heads;
+  float* qbar = reinterpret_cast<float*>(ws + wl.qbar);
+  float* kbar = reinterpret_cast<float*>(ws + wl.kbar);
+  const bool bf16 = dims->dtype == DBSP_BF16;
+  if (dbsp::launch_pool(q, k, qbar, kbar, bh * nqb, bh * nkb, dims->head_dim, bf16, s) !=
+      hipSuccess)
+    return DBSP_ERR_HIP;
+
+  dbsp::SelectArgs a{};
+  a.qbar = qbar;
+  a.kbar = kbar;
+  a.nqb = nqb;
+  a.nkb = nkb;
+  a.scale = score_scale > 0.f ? score_scale : (float)(1.0 / sqrt((double)dims->head_dim));
+  a.t0 = text_blocks.begin;
+  a.t1 = text_blocks.end;
+  a.e0 = dense_extra_blocks.begin;
+  a.e1 = dense_extra_blocks.end;
+  a.mode = mode;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_capacity = col_capacity;
+  a.scores_out = scores_out;
+  a.lds_stride = ((nkb + 63) / 64) * 64 + 16;
+  if (mode == DBSP_TOPK) {
+    int32_t kk, f;
+    topk_k(dims, density_or_mass, text_blocks, dense_extra_blocks, topk_override, &kk, &f);
+    a.kk = kk;
+    a.per_row = f + kk;
+  } else {
+    a.keep_all = density_or_mass >= 1.0;
+    a.theta = (uint64_t)ceil(density_or_mass * 4611686018427387904.0);  // tau * 2^62
+    a.counts = reinterpret_cast<int32_t*>(ws + wl.counts);
+    a.masks = reinterpret_cast<uint64_t*>(ws + wl.masks);
+    a.words = (nkb + 63) / 64;
+  }
+  if (dbsp::launch_select(a, bh, dims->head_dim, s) != hipSuccess) return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
+                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                             float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
+                             void* stream) {
+  if (!shape_ok(dims) || !q || !k || !v || !row_ptr || !o) return DBSP_ERR_INVALID_ARG;
+  if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
+  if (o_dtype != DBSP_F32 && o_dtype != DBSP_BF16) return DBSP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return DBSP_ERR_INVALID_ARG;
+  if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
+  if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
+  const float scale = softmax_scale > 0.f ? softmax_scale
+                                          : (float)(1.0 / sqrt((double)dims->head_dim));
+  dbsp::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_capacity = col_capacity;
+  a.heads = dims->heads;
+  a.nqb = dims->lq / DBSP_BLOCK;
+  a.nkb = dims->lk / DBSP_BLOCK;
+  a.rows = rows_of(dims);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o;
+  a.o_bf16 = o_dtype == DBSP_BF16;
+  a.lse = lse_out;
+  if (dbsp::launch_attn(a, dims->head_dim, dims->dtype == DBSP_BF16,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+}  // extern "C"

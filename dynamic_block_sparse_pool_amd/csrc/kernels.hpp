@@ -1,0 +1,50 @@
+// Launch interface between the host API (api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbsp {
+
+struct SelectArgs {
+  const float* qbar;   // [BH * nqb, D] pooled queries (workspace)
+  const float* kbar;   // [BH * nkb, D] pooled keys (workspace)
+  int nqb, nkb;
+  float scale;         // score scale
+  int t0, t1, e0, e1;  // forced key-block ranges [t0, t1) and [e0, e1)
+  int mode;            // 0 Top-K, 1 mass
+  int kk;              // Top-K: candidates kept per row
+  int per_row;         // Top-K: entries per row (forced + kk)
+  uint64_t theta;      // mass: ceil(tau * 2^62)
+  int keep_all;        // mass: tau >= 1
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int64_t col_capacity;
+  float* scores_out;   // nullable [rows, nkb]
+  int32_t* counts;     // mass: [rows] (workspace)
+  uint64_t* masks;     // mass: [rows, words] (workspace)
+  int words;           // mass: ceil(nkb / 64)
+  int lds_stride;      // floats per score row in LDS
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t col_capacity;
+  int heads, nqb, nkb;
+  int64_t rows;
+  float scale_log2;  // softmax_scale * log2(e)
+  void* o;
+  int o_bf16;
+  float* lse;
+};
+
+hipError_t launch_pool(const void* q, const void* k, float* qbar, float* kbar, int64_t nq_blocks,
+                       int64_t nk_blocks, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream);
+
+}  // namespace dbsp

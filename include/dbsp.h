@@ -1,0 +1,170 @@
+/*
+ * dbsp.h - C ABI of libdbsp.so: per-head dynamic block-sparse attention on gfx950 (MI355X).
+ *
+ * The hot path is two calls:
+ *
+ *   dbsp_sparse_select    Q, K -> for every (batch, head, query block) the key blocks to attend,
+ *                         as a forward-only CSR skip list.
+ *   dbsp_sparse_attn_fwd  Q, K, V, CSR -> O (and optionally the log-sum-exp), attending only
+ *                         to the tokens of the kept key blocks.
+ *
+ * What the calls compute follows two pages:
+ *   [SparSTAR] "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis", in the
+ *       pchao.org digest titled "SparSTAR：为什么视频自回归的稀疏注意力不能跨尺度复用？", section
+ *       "方法概览" (method overview): 128-token blocks, mean-pooled Q and K per block, a pooled
+ *       compatibility score per block pair, clip-aware dense segments (text; in the first clip
+ *       also the image pyramid), a joint Top-K over the remaining key blocks, per-head masks,
+ *       and a forward-only sparse attention path that builds no backward index.
+ *   [CalibAtt] "Accelerating Text-to-Video Generation with Calibrated Sparse Attention"
+ *       (papernotes.org), key design 1 with Eq. (5) (block energy; keep the shortest prefix of
+ *       the energy-sorted row that reaches a threshold, restored to the original order) and
+ *       key design 4 (a read-only per-query-block list of key blocks consumed by the kernel).
+ *
+ * Conventions shared by every call
+ *   Layout     Q is [batch, heads, lq, head_dim]; K and V are [batch, heads, lk, head_dim];
+ *              all contiguous row-major and 16-byte aligned. lq and lk are multiples of 128.
+ *              Block i of a sequence is tokens [128 i, 128 i + 128).
+ *   Rows       CSR row r = (b * heads + h) * (lq / 128) + i for batch b, head h, query block i.
+ *              col_idx of a row lists key-block indices in strictly ascending order.
+ *   Types      dtype DBSP_BF16 (head_dim 128) or DBSP_F32 (head_dim 64 or 128).
+ *   Memory     The caller allocates every buffer (inputs, outputs, CSR, workspace) in device
+ *              memory. The library allocates nothing, frees nothing, keeps no state between
+ *              calls and never writes its inputs. Calls on different streams with disjoint
+ *              output and workspace buffers may overlap.
+ *   Streams    `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work and return
+ *              without waiting for it. nnz is left on the device in row_ptr[rows].
+ *   Errors     Every argument check runs on the host before anything is launched; a negative
+ *              status is returned and no output is touched. DBSP_ERR_HIP reports a failed
+ *              launch. Non-finite input values are not checked: masks and outputs are then
+ *              unspecified. Kernels never read or write outside the buffers described here,
+ *              even for malformed CSR contents (out-of-range column entries are skipped and row
+ *              extents are clipped to col_capacity).
+ */
+#ifndef DBSP_H
+#define DBSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBSP_BLOCK 128          /* tokens per block ([SparSTAR] method overview)          */
+#define DBSP_MAX_KEY_BLOCKS 2048 /* largest lk / 128 supported by dbsp_sparse_select        */
+
+enum {
+  DBSP_OK = 0,
+  DBSP_ERR_INVALID_ARG = -1, /* null pointer, bad shape, range or parameter                  */
+  DBSP_ERR_UNSUPPORTED = -2, /* valid request this build does not implement                  */
+  DBSP_ERR_CAPACITY = -3,    /* col_capacity below the bound from dbsp_select_nnz_bound      */
+  DBSP_ERR_WORKSPACE = -4,   /* workspace missing or smaller than dbsp_select_workspace_bytes */
+  DBSP_ERR_HIP = -5          /* a HIP launch failed                                          */
+};
+
+enum { DBSP_F32 = 0, DBSP_BF16 = 1 };  /* element types                                      */
+enum { DBSP_TOPK = 0, DBSP_MASS = 1 }; /* selection rules                                    */
+
+/* Half-open range [begin, end) of key-block indices; empty when begin == end. */
+typedef struct dbsp_range {
+  int32_t begin;
+  int32_t end;
+} dbsp_range;
+
+/* Problem shape. dtype is DBSP_F32 or DBSP_BF16 and applies to Q, K and V. */
+typedef struct dbsp_dims {
+  int32_t batch;
+  int32_t heads;
+  int32_t lq;
+  int32_t lk;
+  int32_t head_dim;
+  int32_t dtype;
+} dbsp_dims;
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t dbsp_version(void);
+
+/* Human-readable text for a status code; never NULL, static storage. */
+const char* dbsp_status_string(int32_t status);
+
+/*
+ * Number of kept key blocks per row in Top-K mode for a given density: the forced blocks plus
+ * K = min(|C|, ceil(density * |C|)) candidates, |C| = lk / 128 minus the forced count
+ * ([SparSTAR] decreasing density schedule: a density is the kept fraction of the blocks that
+ * are not forced). topk_override >= 0 replaces K (must be <= |C|). Host only.
+ * Writes K to *k_out. Returns DBSP_ERR_INVALID_ARG for a density outside [0, 1], bad ranges or
+ * an override above |C|.
+ */
+int32_t dbsp_topk_budget(const dbsp_dims* dims, double density, dbsp_range text_blocks,
+                         dbsp_range dense_extra_blocks, int32_t topk_override, int32_t* k_out);
+
+/*
+ * Upper bound on nnz for dbsp_sparse_select: exact (rows * (forced + K)) in DBSP_TOPK mode and
+ * rows * (lk / 128) in DBSP_MASS mode. col_idx must hold at least this many entries. Host only.
+ */
+int32_t dbsp_select_nnz_bound(const dbsp_dims* dims, int32_t mode, double density_or_mass,
+                              dbsp_range text_blocks, dbsp_range dense_extra_blocks,
+                              int32_t topk_override, int64_t* nnz_bound);
+
+/* Bytes of device workspace dbsp_sparse_select needs for this shape and mode. Host only. */
+int32_t dbsp_select_workspace_bytes(const dbsp_dims* dims, int32_t mode, uint64_t* bytes);
+
+/*
+ * Selection ([SparSTAR] method overview; [CalibAtt] key design 1).
+ *
+ * For every (batch, head):
+ *   1. qbar_i = mean of the 128 query vectors of block i; kbar_c likewise for key block c.
+ *   2. S_ic = (qbar_i . kbar_c) * score_scale (score_scale <= 0 means 1 / sqrt(head_dim)).
+ *   3. F = text_blocks U dense_extra_blocks is kept in every row (clip-aware retention: text
+ *      always; in the first clip also the image-pyramid range; pass an empty range otherwise).
+ *   4a. DBSP_TOPK: keep K more blocks of C = (all \ F) with the largest S_ic; K comes from
+ *       density_or_mass in [0, 1] as in dbsp_topk_budget. Equal scores go to the lower block
+ *       index; -0.0 equals +0.0.
+ *   4b. DBSP_MASS: p_ic = softmax over all key blocks c of S_ic (fp32). With fixed-point masses
+ *       u = floor(p * 2^62) and threshold ceil(tau * 2^62), tau = density_or_mass in (0, 1]:
+ *       F counts first, then candidates are added in (p descending, index ascending) order
+ *       until the sum reaches the threshold; if it never does, every block is kept; tau = 1
+ *       keeps every block.
+ *   5. row_ptr [rows + 1] (int32, device) receives the exclusive prefix of the per-row counts;
+ *      col_idx [col_capacity] (int32, device) the kept blocks of each row, ascending.
+ *
+ * scores_out, if not NULL, is a device float32 [rows, lk / 128] buffer that receives the exact
+ * values the selection compared: S in Top-K mode and p in mass mode.
+ * workspace must be device memory of at least dbsp_select_workspace_bytes bytes, 256-byte
+ * aligned; its contents on entry do not matter.
+ * Limits: lk / 128 <= DBSP_MAX_KEY_BLOCKS; the nnz bound must fit in int32.
+ */
+int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
+                           dbsp_range text_blocks, dbsp_range dense_extra_blocks, int32_t mode,
+                           double density_or_mass, int32_t topk_override, float score_scale,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                           float* scores_out, void* workspace, uint64_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Block-sparse attention, forward only ([SparSTAR] FastFlex bullet; [CalibAtt] key design 4).
+ *
+ * For each CSR row r = (b, h, i) and each query t of block i:
+ *   o_t   = sum over tokens j of the kept key blocks of softmax_j(q_t . k_j * softmax_scale) v_j
+ *   lse_t = log(sum over the same j of exp(q_t . k_j * softmax_scale))
+ * with softmax_scale <= 0 meaning 1 / sqrt(head_dim), no causal mask, and O = 0, lse = -inf
+ * for a row with no kept block. Arithmetic: bf16 inputs use bf16 matrix-core products with
+ * float32 accumulation and a float32 online softmax (probabilities rounded to bf16 before the
+ * value product); float32 inputs use float32 throughout.
+ *
+ * row_ptr [rows + 1] and col_idx are device int32 arrays as produced by dbsp_sparse_select (or
+ * any CSR with ascending or unordered in-range entries); entries outside [0, lk / 128) are
+ * skipped and row extents are clipped to [0, col_capacity).
+ * o is [batch, heads, lq, head_dim] in o_dtype (DBSP_F32 or DBSP_BF16, round to nearest even).
+ * lse_out, if not NULL, is float32 [batch, heads, lq].
+ */
+int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
+                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                             float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DBSP_H */

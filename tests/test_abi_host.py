@@ -1,0 +1,171 @@
+"""Host-side checks of libdbsp.so: it loads, exports every function include/dbsp.h declares, and
+its argument validation returns the documented status before any GPU work. No call here
+reaches a kernel launch, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from dynamic_block_sparse_pool_amd import _abi
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dbsp.h")
+
+# Aligned, non-null addresses that are never dereferenced: every call below fails validation
+# on the host first.
+FAKE = ctypes.c_void_p(1 << 20)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        from dynamic_block_sparse_pool_amd import build
+        build.build()
+    return _abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dbsp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(lib):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert set(names) == set(_abi.SIGNATURES), "binding signatures differ from the header"
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_exports_with_nm(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(dbsp_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dbsp_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.dbsp_status_string(code).decode() not in ("", "unknown status")
+    assert lib.dbsp_status_string(42).decode() == "unknown status"
+
+
+def dims_of(w, **kw):
+    d = dict(batch=w.batch, heads=w.heads, lq=w.lq, lk=w.lk, head_dim=w.head_dim,
+             dtype=_abi.DBSP_F32 if w.dtype == "f32" else _abi.DBSP_BF16)
+    d.update(kw)
+    return _abi.Dims(**d)
+
+
+@pytest.mark.parametrize("name", ["toy", "star_mid_clip2", "clip1_early", "final_720p_clip2"])
+def test_topk_budget_matches_oracle_reading(lib, name):
+    w = WORKLOADS[name]
+    dims = dims_of(w)
+    out = ctypes.c_int32()
+    assert lib.dbsp_topk_budget(ctypes.byref(dims), w.param, _abi.Range(*w.text),
+                                _abi.Range(*w.extra), -1, ctypes.byref(out)) == 0
+    forced = oracle.forced_blocks(w.n_k_blocks, w.text, w.extra)
+    assert out.value == oracle.topk_budget(w.param, int((~forced).sum()))
+    nnz = ctypes.c_int64()
+    assert lib.dbsp_select_nnz_bound(ctypes.byref(dims), _abi.DBSP_TOPK, w.param,
+                                     _abi.Range(*w.text), _abi.Range(*w.extra), -1,
+                                     ctypes.byref(nnz)) == 0
+    assert nnz.value == w.rows * (int(forced.sum()) + out.value)
+
+
+def test_budget_edge_cases(lib):
+    dims = _abi.Dims(1, 1, 128, 8 * 128, 128, _abi.DBSP_BF16)
+    out = ctypes.c_int32()
+    r0 = _abi.Range(0, 0)
+    assert lib.dbsp_topk_budget(ctypes.byref(dims), 0.0, r0, r0, -1, ctypes.byref(out)) == 0
+    assert out.value == 0
+    assert lib.dbsp_topk_budget(ctypes.byref(dims), 1.0, r0, r0, -1, ctypes.byref(out)) == 0
+    assert out.value == 8
+    assert lib.dbsp_topk_budget(ctypes.byref(dims), 0.3, r0, r0, 5, ctypes.byref(out)) == 0
+    assert out.value == 5
+    for bad_density in (-0.1, 1.5, float("nan")):
+        assert lib.dbsp_topk_budget(ctypes.byref(dims), bad_density, r0, r0, -1,
+                                    ctypes.byref(out)) == _abi.DBSP_ERR_INVALID_ARG
+    assert lib.dbsp_topk_budget(ctypes.byref(dims), 0.5, r0, r0, 9,
+                                ctypes.byref(out)) == _abi.DBSP_ERR_INVALID_ARG
+    # overlapping, reversed and out-of-range forced ranges
+    for t, e in (((0, 3), (2, 4)), ((3, 2), (0, 0)), ((0, 9), (0, 0)), ((-1, 2), (0, 0))):
+        assert lib.dbsp_topk_budget(ctypes.byref(dims), 0.5, _abi.Range(*t), _abi.Range(*e), -1,
+                                    ctypes.byref(out)) == _abi.DBSP_ERR_INVALID_ARG
+
+
+def test_mass_bound_and_workspace(lib):
+    w = WORKLOADS["dit_mass"]
+    dims = dims_of(w)
+    nnz = ctypes.c_int64()
+    r0 = _abi.Range(0, 0)
+    assert lib.dbsp_select_nnz_bound(ctypes.byref(dims), _abi.DBSP_MASS, 0.9, r0, r0, -1,
+                                     ctypes.byref(nnz)) == 0
+    assert nnz.value == w.rows * w.n_k_blocks
+    for bad_tau in (0.0, -0.5, 1.01):
+        assert lib.dbsp_select_nnz_bound(ctypes.byref(dims), _abi.DBSP_MASS, bad_tau, r0, r0, -1,
+                                         ctypes.byref(nnz)) == _abi.DBSP_ERR_INVALID_ARG
+    ws_topk, ws_mass = ctypes.c_uint64(), ctypes.c_uint64()
+    assert lib.dbsp_select_workspace_bytes(ctypes.byref(dims), _abi.DBSP_TOPK, ctypes.byref(ws_topk)) == 0
+    assert lib.dbsp_select_workspace_bytes(ctypes.byref(dims), _abi.DBSP_MASS, ctypes.byref(ws_mass)) == 0
+    pooled = (w.rows + w.batch * w.heads * w.n_k_blocks) * w.head_dim * 4
+    assert ws_topk.value >= pooled and ws_mass.value > ws_topk.value
+
+
+def _select(lib, dims, mode=_abi.DBSP_TOPK, param=0.5, text=(0, 1), extra=(0, 0), q=FAKE, k=FAKE,
+            row_ptr=FAKE, col_idx=FAKE, cap=1 << 40, ws=FAKE, ws_bytes=1 << 40, override=-1):
+    return lib.dbsp_sparse_select(q, k, ctypes.byref(dims), _abi.Range(*text), _abi.Range(*extra),
+                                  mode, param, override, 0.0, row_ptr, col_idx, cap, None, ws,
+                                  ws_bytes, None)
+
+
+def test_select_rejects_bad_arguments(lib):
+    good = _abi.Dims(1, 2, 256, 1024, 128, _abi.DBSP_BF16)
+    E = _abi
+    assert _select(lib, good, q=None) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, k=None) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, row_ptr=None) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, col_idx=None) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, q=ctypes.c_void_p((1 << 20) + 2)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 200, 1024, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(0, 2, 256, 1024, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 256, 1024, 128, 7)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 256, 1024, 96, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+    assert _select(lib, _abi.Dims(1, 1, 256, 2049 * 128, 128, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+    assert _select(lib, good, mode=5) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, param=1.5) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, mode=E.DBSP_MASS, param=0.0) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, text=(0, 3), extra=(2, 5)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, text=(0, 9)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, good, override=8) == E.DBSP_ERR_INVALID_ARG
+    # capacity: 2 heads x 2 query blocks x (1 forced + ceil(0.5 * 7) = 4) = 20 entries
+    assert _select(lib, good, cap=19) == E.DBSP_ERR_CAPACITY
+    assert _select(lib, good, cap=19, mode=E.DBSP_MASS, param=0.9) == E.DBSP_ERR_CAPACITY
+    assert _select(lib, good, ws=None) == E.DBSP_ERR_WORKSPACE
+    assert _select(lib, good, ws_bytes=16) == E.DBSP_ERR_WORKSPACE
+    assert _select(lib, good, ws=ctypes.c_void_p((1 << 20) + 16)) == E.DBSP_ERR_WORKSPACE
+
+
+def test_attn_rejects_bad_arguments(lib):
+    E = _abi
+    good = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_BF16)
+
+    def attn(dims=good, q=FAKE, k=FAKE, v=FAKE, rp=FAKE, ci=FAKE, cap=16, scale=0.0, o=FAKE,
+             odt=E.DBSP_F32):
+        return lib.dbsp_sparse_attn_fwd(q, k, v, ctypes.byref(dims), rp, ci, cap, scale, o, odt,
+                                        None, None)
+
+    for kw in ({"q": None}, {"k": None}, {"v": None}, {"rp": None}, {"o": None}, {"ci": None},
+               {"cap": -1}, {"odt": 3}, {"scale": float("inf")},
+               {"v": ctypes.c_void_p((1 << 20) + 8)},
+               {"dims": _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)}):
+        assert attn(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    assert attn(dims=_abi.Dims(1, 2, 256, 1024, 64, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+    assert attn(dims=_abi.Dims(1, 2, 256, 1024, 32, E.DBSP_F32)) == E.DBSP_ERR_UNSUPPORTED

@@ -1,0 +1,87 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Every mask row is checked bit-exact against the oracle selecting from the GPU's own scores.
+Pooled scores are checked against the oracle's pooling on sampled heads; attention outputs on
+sampled rows (first, last, and seeded random rows), each computed by the oracle one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, make_qkv
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-full] {msg}", flush=True)
+
+
+def head_host(t, b, h):
+    return P.host(t[b:b + 1, h:h + 1])
+
+
+@pytest.mark.parametrize("name", ["star_mid_clip2", "clip1_early", "final_720p_clip2", "dit_mass"])
+def test_full_size(name):
+    import dynamic_block_sparse_pool_amd as dbsp
+    w = WORKLOADS[name]
+    say(f"case {name}: H={w.heads} Lq={w.lq} Lk={w.lk} {w.mode}={w.param}")
+    q, k, v = make_qkv(w, device="cuda", seed=0)
+    kw = dict(density=w.param) if w.mode == "topk" else dict(mass=w.param)
+    plan = dbsp.SelectPlan(q, k, w.text, w.extra, return_scores=True, **kw)
+    idx = plan.run(q, k)
+    o = dbsp.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32)
+    o16 = dbsp.sparse_attn_fwd(q, k, v, idx)          # the bf16 output the benchmark times
+    torch.cuda.synchronize()
+    nkb, nqb = w.n_k_blocks, w.n_q_blocks
+    rp = idx.row_ptr.cpu().numpy().astype(np.int64)
+    ci = idx.col_idx.cpu().numpy().astype(np.int64)
+    scores = idx.scores.cpu().numpy().astype(np.float64)
+    say(f"  nnz {int(rp[-1])} executed density {rp[-1] / (w.rows * nkb):.4f}")
+
+    # masks: every row, bit-exact on the GPU's scores
+    forced = oracle.forced_blocks(nkb, w.text, w.extra)
+    kept_gpu = P.csr_to_kept_fast(rp, ci, nkb)
+    if w.mode == "topk":
+        kk = oracle.topk_budget(w.param, int((~forced).sum()))
+        kept_ora = oracle.select_topk(scores, forced, kk)
+    else:
+        kept_ora = oracle.select_mass(scores, forced, w.param)
+    np.testing.assert_array_equal(kept_gpu, kept_ora)
+    say("  masks bit-exact on all rows")
+
+    # pooled scores / energies on sampled heads
+    scale = 1.0 / math.sqrt(w.head_dim)
+    rng = np.random.default_rng(1234)
+    heads = sorted({0, w.heads - 1, int(rng.integers(1, w.heads - 1))})
+    s4 = scores.reshape(w.batch, w.heads, nqb, nkb)
+    for h in heads:
+        qbar = oracle.pool(head_host(q, 0, h))[0, 0]
+        kbar = oracle.pool(head_host(k, 0, h))[0, 0]
+        if w.mode == "topk":
+            P.check_scores(s4[0, h], qbar, kbar, scale)
+        else:
+            P.check_energies(s4[0, h], oracle.block_softmax(oracle.block_scores(qbar, kbar, scale)))
+    say(f"  scores checked on heads {heads}")
+
+    # attention on sampled rows
+    rows = sorted({0, w.rows - 1, *rng.integers(0, w.rows, size=6).tolist()})
+    worst = 0.0
+    for r in rows:
+        b, rest = divmod(r, w.heads * nqb)
+        h, i = divmod(rest, nqb)
+        qh, kh, vh = head_host(q, b, h), head_host(k, b, h), head_host(v, b, h)
+        cols = ci[rp[r]:rp[r + 1]]
+        rp_h = np.zeros(nqb + 1, np.int64)
+        rp_h[i + 1:] = cols.size                      # only row i of this head has entries
+        o_ref, lse_ref = oracle.attention_rows(qh, kh, vh, rp_h, cols, rows=[i], scale=scale)
+        o_g = P.host(o[b, h, i * P.BLOCK:(i + 1) * P.BLOCK])
+        mx, _ = P.check_attention(o_g[None], None, o_ref, lse_ref, True)
+        worst = max(worst, mx)
+        o16_g = P.host(o16[b, h, i * P.BLOCK:(i + 1) * P.BLOCK])
+        assert np.array_equal(o16_g, P.host(torch.from_numpy(o_g.astype(np.float32)).to(torch.bfloat16)))
+    say(f"  attention rows {rows}: worst max err {worst:.2e}")
