@@ -25,45 +25,140 @@
 
 namespace dbsp {
 
-constexpr int kKStride = 136;  // bf16 per K row in LDS (272 B: 16 consecutive rows hit distinct banks)
-constexpr int kVStride = 160;  // bf16 per V row in LDS (320 B: transpose reads are conflict free)
+// LDS tiles hold one key block of K or V (128 rows x 256 bytes) unpadded. Global-to-LDS DMA
+// writes 1 KiB per wave instruction contiguously, so bank conflicts are avoided by an XOR
+// swizzle of the 16-byte chunk index within each row instead of padding:
+//   K: physical chunk = c ^ (row & 15)      (16 consecutive rows read at one logical chunk)
+//   V: physical chunk = c ^ (4 * (row & 3))  (transpose reads: 4 rows x 4 chunks per half wave)
+__device__ __forceinline__ int k_swz(int row, int chunk) { return chunk ^ (row & 15); }
+__device__ __forceinline__ int v_swz(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+// Workgroup barrier without the implicit drain of outstanding vector-memory operations that a
+// fenced barrier would add (the K/V prefetch must stay in flight across it). The empty asm
+// statements keep the compiler from moving memory accesses across the barrier; the waits the
+// algorithm needs are issued explicitly next to each barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane byte offsets (inside a 4-row, 1 KiB slab) of the global source of a tile DMA. For
+// slab i (rows 4 i .. 4 i + 3 of the wave's 32) the swizzle depends on the row only modulo 16
+// (K) or 4 (V), so K needs four offsets (i mod 4) and V one.
+struct DmaOffsets {
+  uint32_t k[4];
+  uint32_t v;
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+  DmaOffsets d;
+  const int r = lane >> 4, pc = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d.k[i] = (uint32_t)(r * 256 + k_swz(4 * i + r, pc) * 16);
+  d.v = (uint32_t)(r * 256 + v_swz(r, pc) * 16);
+  return d;
+}
+
+// Issue the DMA of one 128 x 128 bf16 tile (32 KiB at `tile`, wave-uniform) into LDS: wave w
+// copies rows 32 w .. 32 w + 31, one 4-row slab (1 KiB) per instruction, lane l landing at byte
+// 16 l of the slab, so the swizzle is applied on the global side.
+template <bool kIsV>
+__device__ __forceinline__ void tile_dma(const char* tile, uint16_t* lds, int w,
+                                         const DmaOffsets& d) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slab = 32 * w + 4 * i;  // first row of the slab
+    const char* src = tile + slab * 256 + (kIsV ? d.v : d.k[i & 3]);
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + slab * 128), 16, 0, 0);
+  }
+}
 
 __device__ __forceinline__ int64_t clip64(int64_t x, int64_t lo, int64_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBlock * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kBlock * kVStride];
+constexpr int kListCap = 2048;  // kept-block indices staged in LDS per window
+
+// Copy the in-range entries of col_idx[*pos, end) into list in their original order, 256
+// entries per pass (wave w takes the w-th 64), stopping before a pass that could overflow
+// kListCap. Advances *pos past the entries consumed and returns how many were kept. All four
+// waves take part; the result is visible to all of them on return.
+__device__ __forceinline__ int stage_list(const int32_t* __restrict__ col_idx, int64_t* pos,
+                                          int64_t end, int nkb, int* list, int* wave_cnt,
+                                          int tid) {
+  const int lane = tid & 63, w = tid >> 6;
+  int total = 0;
+  int64_t p = *pos;
+  while (p < end && total + 256 <= kListCap) {
+    const int64_t e = p + 64 * w + lane;
+    const int c = e < end ? col_idx[e] : -1;
+    const bool ok = c >= 0 && c < nkb;
+    const uint64_t m = __ballot(ok);
+    if (lane == 0) wave_cnt[w] = __popcll(m);
+    __syncthreads();
+    int before = total;
+    for (int i = 0; i < w; ++i) before += wave_cnt[i];
+    if (ok) list[before + mbcnt64(m)] = c;
+    total += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    p += 256;
+    __syncthreads();
+  }
+  *pos = p < end ? p : end;
+  return total;
+}
+
+// Pointers are separate __restrict__ parameters and the kept-block indices are staged in LDS:
+// a vector load of an index inside the pipelined loop would need a vector-memory wait that
+// drains the K/V prefetch.
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
+    const uint16_t* __restrict__ vg, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, int64_t col_capacity, int nqb, int nkb,
+    float scale_log2, void* __restrict__ o, int o_bf16, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kBlock * 128];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kBlock * 128];
+  __shared__ int list[kListCap];
+  __shared__ int wave_cnt[8];
 
   const int64_t row = blockIdx.x;
-  const int64_t bh = row / a.nqb;
-  const int qb = (int)(row - bh * a.nqb);
+  const int64_t bh = row / nqb;
+  const int qb = (int)(row - bh * nqb);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int64_t lq = (int64_t)a.nqb * kBlock;
-  const int64_t lk = (int64_t)a.nkb * kBlock;
+  const int64_t lq = (int64_t)nqb * kBlock;
+  const int64_t lk = (int64_t)nkb * kBlock;
 
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + bh * lk * 128;
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + bh * lk * 128;
+  const char* kp = reinterpret_cast<const char*>(kg + bh * lk * 128);
+  const char* vp = reinterpret_cast<const char*>(vg + bh * lk * 128);
+  const DmaOffsets dmo = dma_offsets(lane);
+  constexpr int64_t kTileBytes = (int64_t)kBlock * 128 * 2;
 
   // Q^T as the B operand of S^T = K Q^T: lane (h, l32) holds query 32 w + l32, dims 16 s + 8 h .. +7
   const int64_t qtok = bh * lq + (int64_t)qb * kBlock + 32 * w + l32;
   bf16x8 qf[8];
   {
-    const uint16_t* qr = qp + qtok * 128 + 8 * h;
+    const uint16_t* qr = qg + qtok * 128 + 8 * h;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
   }
 
-  int64_t beg = a.row_ptr[row], end = a.row_ptr[row + 1];
-  beg = clip64(beg, 0, a.col_capacity);
-  end = clip64(end, beg, a.col_capacity);
+  int64_t pos = clip64(row_ptr[row], 0, col_capacity);
+  const int64_t end = clip64(row_ptr[row + 1], pos, col_capacity);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -73,111 +168,123 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // per-thread coordinates for the cooperative K / V copies: 8 passes of 16 rows x 16 chunks
-  const int cp_row = tid >> 4;
-  const int cp_chunk = tid & 15;
-  // per-lane coordinates for the transposed V reads
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  for (int64_t it = beg; it < end; ++it) {
-    const int cb = a.col_idx[it];
-    if (cb < 0 || cb >= a.nkb) continue;
-    const uint16_t* kb = kp + (int64_t)cb * kBlock * 128;
-    const uint16_t* vb = vp + (int64_t)cb * kBlock * 128;
-    u32x4 kr[8], vr[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r = cp_row + 16 * p;
-      kr[p] = load_u32x4(kb + r * 128 + cp_chunk * 8);
-      vr[p] = load_u32x4(vb + r * 128 + cp_chunk * 8);
+  while (pos < end) {
+    const int n = stage_list(col_idx, &pos, end, nkb, list, wave_cnt, tid);
+    if (n == 0) continue;
+    {
+      const int cb = __builtin_amdgcn_readfirstlane(list[0]);
+      tile_dma<false>(kp + cb * kTileBytes, k_lds, w, dmo);
+      tile_dma<true>(vp + cb * kTileBytes, v_lds, w, dmo);
     }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r = cp_row + 16 * p;
-      *reinterpret_cast<u32x4*>(k_lds + r * kKStride + cp_chunk * 8) = kr[p];
-      *reinterpret_cast<u32x4*>(v_lds + r * kVStride + cp_chunk * 8) = vr[p];
-    }
-    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+      const bool more = i + 1 < n;
 
-    // S^T tiles: sacc[jt] covers keys 32 jt .. 32 jt + 31 (rows) x this wave's 32 queries
-    f32x16 sacc[4];
+      // K(i) landed in every wave's part (V(i) may still be in flight)
+      wait_vmcnt<8>();
+      wg_barrier();
+
+      // S^T tiles: sacc[jt] covers keys 32 jt .. 32 jt + 31 (rows) x this wave's 32 queries
+      f32x16 sacc[4];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
+      for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
-      const uint16_t* kr0 = k_lds + (32 * jt + l32) * kKStride + 8 * h;
+        for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
+        const int kr = 32 * jt + l32;
+        const uint16_t* krow = k_lds + kr * 128;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + k_swz(kr, 2 * s + h) * 8);
+          sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[jt], 0, 0, 0);
+        }
+      }
+      // the prefetch is unconditional (the last iteration re-fetches its own block): a
+      // conditional DMA makes the compiler's wait bookkeeping drain all pending DMAs
+      const int cb_next = __builtin_amdgcn_readfirstlane(list[more ? i + 1 : i]);
+      wait_lgkmcnt0();
+      wg_barrier();  // every wave is done reading K(i)
+      tile_dma<false>(kp + cb_next * kTileBytes, k_lds, w, dmo);
+
+      // online softmax for query column l32 (lanes l32 and l32 + 32 share it), exp2 domain
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float psum = 0.f;
+      bf16x8 pf[8];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -m_new));
+          psum += p;
+          pf[2 * jt + (r >> 3)][r & 7] = (__bf16)p;
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (__ballot(alpha != 1.0f) != 0ull) {  // the running max moved for some query of the wave
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nt][r] *= alpha;
+      }
+
+      // V(i) landed (the K prefetch just issued may still be in flight)
+      wait_vmcnt<8>();
+      wg_barrier();
+
+      // O^T += V^T P^T; k step s covers keys 16 s .. 16 s + 15 in the accumulator order of S^T
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr0 + 16 * s);
-        sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[jt], 0, 0, 0);
+        const int jb = 16 * s + 4 * h + tr_row;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int col = 32 * nt + tr_col;
+          const int off_lo = jb * 128 + v_swz(jb, col >> 3) * 8 + (col & 7);
+          const int off_hi = (jb + 8) * 128 + v_swz(jb + 8, col >> 3) * 8 + (col & 7);
+          // whole-vector casts only: an element-wise rebuild of these results has been seen to
+          // lose the upper dword of each read in the generated code
+          const u32x2 lo = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_lo)));
+          const u32x2 hi = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_hi)));
+          const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
+                                                             pf[s], oacc[nt], 0, 0, 0);
+        }
       }
+      wait_lgkmcnt0();
+      wg_barrier();  // every wave is done reading V(i)
+      tile_dma<true>(vp + cb_next * kTileBytes, v_lds, w, dmo);
     }
-
-    // online softmax for query column l32 (lanes l32 and l32 + 32 share it)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.f;
-    bf16x8 pf[8];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], a.scale_log2, -m_new));
-        psum += p;
-        pf[2 * jt + (r >> 3)][r & 7] = (__bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[nt][r] *= alpha;
-
-    // O^T += V^T P^T; k step s covers keys 16 s .. 16 s + 15 in the accumulator order of S^T
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int jb = 16 * s + 4 * h + tr_row;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = 32 * nt + tr_col;
-        // whole-vector casts only: an element-wise rebuild of these results has been seen to
-        // lose the upper dword of each read in the generated code
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(v_lds + jb * kVStride + col)));
-        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(v_lds + (jb + 8) * kVStride + col)));
-        const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, w4);
-        oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[s], oacc[nt], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+    wait_vmcnt<0>();
   }
 
   // epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (a.o_bf16) {
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + qtok * 128;
+  if (o_bf16) {
+    uint16_t* orow = static_cast<uint16_t*>(o) + qtok * 128;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n0 = 32 * nt + 8 * g + 4 * h;
         u32x2 pk;
-        pk[0] = f32_to_bf16_bits(oacc[nt][4 * g] * inv) | (f32_to_bf16_bits(oacc[nt][4 * g + 1] * inv) << 16);
-        pk[1] = f32_to_bf16_bits(oacc[nt][4 * g + 2] * inv) | (f32_to_bf16_bits(oacc[nt][4 * g + 3] * inv) << 16);
+        pk[0] = f32_to_bf16_bits(oacc[nt][4 * g] * inv) |
+                (f32_to_bf16_bits(oacc[nt][4 * g + 1] * inv) << 16);
+        pk[1] = f32_to_bf16_bits(oacc[nt][4 * g + 2] * inv) |
+                (f32_to_bf16_bits(oacc[nt][4 * g + 3] * inv) << 16);
         *reinterpret_cast<u32x2*>(orow + n0) = pk;
       }
   } else {
-    float* orow = static_cast<float*>(a.o) + qtok * 128;
+    float* orow = static_cast<float*>(o) + qtok * 128;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -189,8 +296,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4*>(orow + n0) = ov;
       }
   }
-  if (a.lse && h == 0)
-    a.lse[qtok] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  if (lse && h == 0)
+    lse[qtok] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
 template <int D>
@@ -272,7 +379,10 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   dim3 grid((unsigned)a.rows);
   if (bf16 && head_dim == 128)
-    attn_fwd_bf16_kernel<<<grid, 256, 0, stream>>>(a);
+    attn_fwd_bf16_kernel<<<grid, 256, 0, stream>>>(
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+        static_cast<const uint16_t*>(a.v), a.row_ptr, a.col_idx, a.col_capacity, a.nqb, a.nkb,
+        a.scale_log2, a.o, a.o_bf16, a.lse);
   else if (!bf16 && head_dim == 64)
     attn_fwd_f32_kernel<64><<<grid, 128, 0, stream>>>(a);
   else if (!bf16 && head_dim == 128)
