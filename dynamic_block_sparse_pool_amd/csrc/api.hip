@@ -88,6 +88,14 @@ int32_t nnz_bound(const dbsp_dims* d, int32_t mode, double param, dbsp_range t, 
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
 
+// Floats per score row in LDS: at least nkb, rounded to 16, and congruent to 16 or 48 modulo 64
+// so that the four rows an MFMA output spans fall in distinct banks.
+int score_lds_stride(int nkb) {
+  int s = (nkb + 15) & ~15;
+  while ((s & 63) != 16 && (s & 63) != 48) s += 16;
+  return s;
+}
+
 struct WorkspaceLayout {
   uint64_t qbar, kbar, counts, masks, total;
 };
@@ -97,10 +105,11 @@ WorkspaceLayout layout_of(const dbsp_dims* d, int32_t mode) {
   const uint64_t bh = (uint64_t)d->batch * d->heads;
   const uint64_t nqb = d->lq / DBSP_BLOCK, nkb = d->lk / DBSP_BLOCK;
   uint64_t off = 0;
+  // pooled keys, each stored as bf16 hi and lo halves (2 x head_dim x 2 bytes); the pooled
+  // queries never leave the selection kernel
   w.qbar = off;
-  off = align256(off + bh * nqb * d->head_dim * sizeof(float));
-  w.kbar = off;
-  off = align256(off + bh * nkb * d->head_dim * sizeof(float));
+  w.kbar = off;  // tiles of 16 key blocks (the last one padded)
+  off = align256(off + bh * ((nkb + 15) / 16) * 16 * d->head_dim * 2 * sizeof(uint16_t));
   if (mode == DBSP_MASS) {
     w.counts = off;
     off = align256(off + bh * nqb * sizeof(int32_t));
@@ -177,16 +186,15 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t bh = (int64_t)dims->batch * dims->heads;
-  float* qbar = reinterpret_cast<float*>(ws + wl.qbar);
-  float* kbar = reinterpret_cast<float*>(ws + wl.kbar);
+  uint16_t* ksplit = reinterpret_cast<uint16_t*>(ws + wl.kbar);
   const bool bf16 = dims->dtype == DBSP_BF16;
-  if (dbsp::launch_pool(q, k, qbar, kbar, bh * nqb, bh * nkb, dims->head_dim, bf16, s) !=
+  if (dbsp::launch_pool(nullptr, k, nullptr, ksplit, 0, bh * nkb, nkb, dims->head_dim, bf16, s) !=
       hipSuccess)
     return DBSP_ERR_HIP;
 
   dbsp::SelectArgs a{};
-  a.qbar = qbar;
-  a.kbar = kbar;
+  a.q = q;
+  a.ksplit = ksplit;
   a.nqb = nqb;
   a.nkb = nkb;
   a.scale = score_scale > 0.f ? score_scale : (float)(1.0 / sqrt((double)dims->head_dim));
@@ -199,7 +207,8 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
   a.col_idx = col_idx;
   a.col_capacity = col_capacity;
   a.scores_out = scores_out;
-  a.lds_stride = ((nkb + 63) / 64) * 64 + 16;
+  a.lds_stride = score_lds_stride(nkb);
+  a.n_rows = bh * nqb;
   if (mode == DBSP_TOPK) {
     int32_t kk, f;
     topk_k(dims, density_or_mass, text_blocks, dense_extra_blocks, topk_override, &kk, &f);
@@ -212,7 +221,7 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
     a.masks = reinterpret_cast<uint64_t*>(ws + wl.masks);
     a.words = (nkb + 63) / 64;
   }
-  if (dbsp::launch_select(a, bh, dims->head_dim, s) != hipSuccess) return DBSP_ERR_HIP;
+  if (dbsp::launch_select(a, bh, dims->head_dim, bf16, s) != hipSuccess) return DBSP_ERR_HIP;
   return DBSP_OK;
 }
 

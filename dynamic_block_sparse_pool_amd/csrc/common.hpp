@@ -48,6 +48,98 @@ __device__ __forceinline__ int mbcnt64(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
+// Cross-lane steps through DPP (no LDS round trip). dpp<CTRL, ROW_MASK>(v) returns v moved as
+// CTRL says, and 0 in lanes with no source or in rows outside ROW_MASK.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes (lane i gets the sum of lanes 0..i).
+__device__ __forceinline__ uint32_t wave_prefix_sum_u32(uint32_t v) {
+  v += dpp_u32<kRowShr1>(v);
+  v += dpp_u32<kRowShr2>(v);
+  v += dpp_u32<kRowShr4>(v);
+  v += dpp_u32<kRowShr8>(v);
+  v += dpp_u32<kRowBcast15, 0xa>(v);
+  v += dpp_u32<kRowBcast31, 0xc>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_prefix_sum_u64(uint64_t v) {
+#define DBSP_ADD64(CTRL, MASK)                                                               \
+  v += ((uint64_t)dpp_u32<CTRL, MASK>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL, MASK>((uint32_t)v);
+  DBSP_ADD64(kRowShr1, 0xf)
+  DBSP_ADD64(kRowShr2, 0xf)
+  DBSP_ADD64(kRowShr4, 0xf)
+  DBSP_ADD64(kRowShr8, 0xf)
+  DBSP_ADD64(kRowBcast15, 0xa)
+  DBSP_ADD64(kRowBcast31, 0xc)
+#undef DBSP_ADD64
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Wave-wide reductions through the prefix scan; the result is wave-uniform.
+__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v) {
+  v = wave_prefix_sum_u64(v);
+  return ((uint64_t)lane_u32((uint32_t)(v >> 32), 63) << 32) | lane_u32((uint32_t)v, 63);
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_fill_u32(uint32_t v, uint32_t fill) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Wave-wide max / sum / min through the same scan pattern; the results are wave-uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<kRowShr1>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowShr2>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowShr4>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowShr8>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowBcast15, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp_f32<kRowBcast31, 0xc>(v, -INFINITY));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_total_f32(float v) {
+  v += dpp_f32<kRowShr1>(v, 0.f);
+  v += dpp_f32<kRowShr2>(v, 0.f);
+  v += dpp_f32<kRowShr4>(v, 0.f);
+  v += dpp_f32<kRowShr8>(v, 0.f);
+  v += dpp_f32<kRowBcast15, 0xa>(v, 0.f);
+  v += dpp_f32<kRowBcast31, 0xc>(v, 0.f);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+  v = min(v, dpp_fill_u32<kRowShr1>(v, 0xffffffffu));
+  v = min(v, dpp_fill_u32<kRowShr2>(v, 0xffffffffu));
+  v = min(v, dpp_fill_u32<kRowShr4>(v, 0xffffffffu));
+  v = min(v, dpp_fill_u32<kRowShr8>(v, 0xffffffffu));
+  v = min(v, dpp_fill_u32<kRowBcast15, 0xa>(v, 0xffffffffu));
+  v = min(v, dpp_fill_u32<kRowBcast31, 0xc>(v, 0xffffffffu));
+  return lane_u32(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, dpp_fill_u32<kRowShr1>(v, 0u));
+  v = max(v, dpp_fill_u32<kRowShr2>(v, 0u));
+  v = max(v, dpp_fill_u32<kRowShr4>(v, 0u));
+  v = max(v, dpp_fill_u32<kRowShr8>(v, 0u));
+  v = max(v, dpp_fill_u32<kRowBcast15, 0xa>(v, 0u));
+  v = max(v, dpp_fill_u32<kRowBcast31, 0xc>(v, 0u));
+  return lane_u32(v, 63);
+}
+
 __device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -7,8 +7,9 @@
 namespace dbsp {
 
 struct SelectArgs {
-  const float* qbar;   // [BH * nqb, D] pooled queries (workspace)
-  const float* kbar;   // [BH * nkb, D] pooled keys (workspace)
+  const void* q;           // queries [BH, nqb * 128, D] (bf16 or fp32), pooled in the kernel
+  const uint16_t* ksplit;  // pooled keys as bf16 hi | lo in MFMA tile order (workspace):
+                           // [BH][ceil(nkb / 16)][D / 32][hi | lo][64 lanes][8]
   int nqb, nkb;
   float scale;         // score scale
   int t0, t1, e0, e1;  // forced key-block ranges [t0, t1) and [e0, e1)
@@ -25,6 +26,7 @@ struct SelectArgs {
   uint64_t* masks;     // mass: [rows, words] (workspace)
   int words;           // mass: ceil(nkb / 64)
   int lds_stride;      // floats per score row in LDS
+  int64_t n_rows;      // batch * heads * nqb
 };
 
 struct AttnArgs {
@@ -42,9 +44,11 @@ struct AttnArgs {
   float* lse;
 };
 
-hipError_t launch_pool(const void* q, const void* k, float* qbar, float* kbar, int64_t nq_blocks,
-                       int64_t nk_blocks, int head_dim, bool bf16, hipStream_t stream);
-hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, hipStream_t stream);
+hipError_t launch_pool(const void* q, const void* k, uint16_t* qsplit, uint16_t* ksplit,
+                       int64_t nq_blocks, int64_t nk_blocks, int nkb, int head_dim, bool bf16,
+                       hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, bool bf16,
+                         hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream);
 
 }  // namespace dbsp

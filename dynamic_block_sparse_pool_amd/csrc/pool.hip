@@ -5,19 +5,32 @@
 // the rest read K blocks; a block is 128 consecutive rows of head_dim elements, contiguous in
 // memory (32 KiB for bf16 x 128 or fp32 x 64). Each of the 256 threads owns one 16-byte column
 // chunk of 128 / (256 / chunks) rows, issues all of its loads before any arithmetic, sums in
-// fp32, and the partial column sums meet in LDS. Output: fp32 [blocks, head_dim] means.
-// HBM-bound: every input byte is read exactly once.
+// fp32, and the partial column sums meet in LDS. Output per block: the fp32 mean m split as
+// hi = bf16(m) and lo = bf16(m - hi): queries as [hi(head_dim) | lo(head_dim)] bf16 per block,
+// keys in the tiled operand order of the scoring MFMAs (see ktile_offset). HBM-bound: every input byte is read exactly once.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dbsp {
 
+// Pooled keys are stored in the operand order of the scoring MFMAs (16x16x32 bf16, B operand):
+// key block n of a (batch, head) with nkb blocks sits in tile t = n / 16 at lane
+// l = 16 * kq + (n % 16) of k step ks, where dim d = 32 ks + 8 kq + e. A tile is
+// [ks][hi | lo][64 lanes][8] bf16 (D / 32 * 2 KiB), so one wave-wide 16-byte load per
+// (ks, hi | lo) reads 1 KiB contiguously.
+template <int D>
+__device__ __forceinline__ int64_t ktile_offset(int64_t bh, int n, int ntiles, int d, int hl) {
+  const int t = n >> 4, m = n & 15;
+  const int ks = d >> 5, kq = (d >> 3) & 3, e = d & 7;
+  return ((((bh * ntiles + t) * (D / 32) + ks) * 2 + hl) * 64 + 16 * kq + m) * 8 + e;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ q,
                                                           const T* __restrict__ k,
-                                                          float* __restrict__ qbar,
-                                                          float* __restrict__ kbar,
-                                                          int64_t nq_blocks) {
+                                                          uint16_t* __restrict__ qbar,
+                                                          uint16_t* __restrict__ kbar,
+                                                          int64_t nq_blocks, int nkb) {
   constexpr int kVec = 16 / (int)sizeof(T);       // elements per 16-byte chunk
   constexpr int kChunks = D / kVec;               // chunks per row
   constexpr int kRowsPerPass = 256 / kChunks;     // rows covered by one pass of the workgroup
@@ -28,15 +41,9 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
 
   int64_t g = blockIdx.x;
   const T* src;
-  float* dst;
-  if (g < nq_blocks) {
-    src = q + g * (int64_t)kBlock * D;
-    dst = qbar + g * D;
-  } else {
-    g -= nq_blocks;
-    src = k + g * (int64_t)kBlock * D;
-    dst = kbar + g * D;
-  }
+  const bool is_q = g < nq_blocks;
+  if (!is_q) g -= nq_blocks;
+  src = (is_q ? q : k) + g * (int64_t)kBlock * D;
   const int t = threadIdx.x;
   const int chunk = t % kChunks;
   const int row0 = t / kChunks;
@@ -70,25 +77,38 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < kRowsPerPass; ++r) s += partial[r][col];
-    dst[col] = s * (1.0f / kBlock);
+    const float m = s * (1.0f / kBlock);
+    const uint32_t hi = f32_to_bf16_bits(m);
+    const uint16_t lo = (uint16_t)f32_to_bf16_bits(m - __uint_as_float(hi << 16));
+    if (is_q) {
+      qbar[g * 2 * D + col] = (uint16_t)hi;
+      qbar[g * 2 * D + D + col] = lo;
+    } else {
+      const int64_t bh = g / nkb;
+      const int n = (int)(g - bh * nkb);
+      const int ntiles = (nkb + 15) >> 4;
+      kbar[ktile_offset<D>(bh, n, ntiles, col, 0)] = (uint16_t)hi;
+      kbar[ktile_offset<D>(bh, n, ntiles, col, 1)] = lo;
+    }
   }
 }
 
-hipError_t launch_pool(const void* q, const void* k, float* qbar, float* kbar, int64_t nq_blocks,
-                       int64_t nk_blocks, int head_dim, bool bf16, hipStream_t stream) {
+hipError_t launch_pool(const void* q, const void* k, uint16_t* qbar, uint16_t* kbar,
+                       int64_t nq_blocks, int64_t nk_blocks, int nkb, int head_dim, bool bf16,
+                       hipStream_t stream) {
   dim3 grid((unsigned)(nq_blocks + nk_blocks)), block(256);
   if (bf16 && head_dim == 128)
     pool_blocks_kernel<uint16_t, 128><<<grid, block, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, nq_blocks);
+        (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, nq_blocks, nkb);
   else if (bf16 && head_dim == 64)
     pool_blocks_kernel<uint16_t, 64><<<grid, block, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, nq_blocks);
+        (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, nq_blocks, nkb);
   else if (!bf16 && head_dim == 64)
     pool_blocks_kernel<float, 64><<<grid, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                               qbar, kbar, nq_blocks);
+                                                               qbar, kbar, nq_blocks, nkb);
   else if (!bf16 && head_dim == 128)
     pool_blocks_kernel<float, 128><<<grid, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                                qbar, kbar, nq_blocks);
+                                                                qbar, kbar, nq_blocks, nkb);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -7,18 +7,26 @@
 // Attention", key design 1 and Eq. (5) (shortest energy-sorted prefix reaching a threshold,
 // restored to block order) and key design 4 (per-query-block skip list).
 //
-// score_select_kernel: one workgroup (4 waves) owns 16 consecutive query blocks of one
-// (batch, head). Phase 1 computes S = qbar kbar^T * scale for its 16 rows against every key
-// block with 16x16x32 bf16 MFMAs on a hi/lo split of the fp32 operands
-// (x = hi + lo, hi = bf16(x), lo = bf16(x - hi); S ~ hi.hi + hi.lo + lo.hi, relative error
-// near 2^-16 of |qbar||kbar|), and parks the 16 score rows in LDS. Phase 2 gives each wave
-// four rows; a wave holds one row in registers (lane l, slot e -> key block 64 e + l) and
-// finds the selection threshold by an MSB-first bitwise search over order-preserving uint32
-// keys, using wave ballots (Top-K: counts) or 64-bit wave sums of fixed-point masses (mass).
-// Keys above the threshold are kept, and keys equal to it in ascending block order until the
-// count or mass is met: the same set a stable (value desc, index asc) sort prefix gives.
-// Emitting kept flags slot by slot with mbcnt yields col_idx already ascending.
-//
+// score_select_kernel: one workgroup (8 waves) owns 16 consecutive query blocks of one
+// (batch, head).
+//   Phase 0 mean-pools those 16 query blocks straight from Q (the pooling kernel handles the
+//   keys, which every workgroup of the head needs before it can score). Streaming Q here lets
+//   the query traffic overlap the latency-bound scoring and selection of other workgroups.
+//   Phase 1 computes S = qbar kbar^T * scale for the 16 rows against every key block with
+//   16x16x32 bf16 MFMAs on the hi/lo split of the pooled vectors written by the pooling kernel
+//   (x = hi + lo; S ~ hi.hi + hi.lo + lo.hi accumulated in fp32, relative error near 2^-16 of
+//   |qbar||kbar|). Pooled keys arrive in MFMA operand order, so each operand load is one
+//   contiguous 1 KiB read per wave. Each wave walks key tiles of 16 with the next tile's
+//   operands in flight, and parks the scores in LDS.
+//   Phase 2 gives each wave two rows. A wave holds one row in registers (lane l, slot e -> key
+//   block 64 e + l), maps scores to order-preserving uint32 keys and finds the selection
+//   threshold T most significant bits first: in Top-K mode by radix select on bytes with a
+//   per-wave LDS histogram (stopping when a bucket holds exactly the remaining count), in mass
+//   mode by a bitwise search on 64-bit mass sums that starts below the common high bits of the
+//   smallest and largest candidate key (T lies between them). Keys above T are kept, and keys
+//   equal to T in ascending block order until the count (Top-K) or mass (mass mode) is met:
+//   the same set as the prefix of a stable (value desc, index asc) sort. Kept flags are
+//   emitted slot by slot with mbcnt, so col_idx comes out ascending.
 // Top-K rows all have |F| + K entries, so row_ptr is written in closed form. Mass rows vary:
 // the kernel stores a per-row bitmask and count, scan_counts_kernel forms row_ptr, and
 // fill_csr_kernel expands the bitmasks into col_idx.
@@ -28,32 +36,23 @@
 namespace dbsp {
 
 constexpr int kRowsPerWG = 16;
+constexpr int kWaves = 8;
 constexpr uint32_t kMassBits = 62;
-
-
-__device__ __forceinline__ void split_bf16(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 h = (__bf16)x[e];
-    hi[e] = h;
-    lo[e] = (__bf16)(x[e] - (float)h);
-  }
-}
 
 // Exact floor(p * 2^62) for a non-negative finite float p < 2.
 __device__ __forceinline__ uint64_t mass_units(float p) {
-  uint32_t u = __float_as_uint(p);
-  int ex = (int)((u >> 23) & 0xffu);
+  const uint32_t u = __float_as_uint(p);
+  const int ex = (int)((u >> 23) & 0xffu);
   if (ex == 0) return 0;  // zero or subnormal: below 2^-126, far below one unit
-  uint64_t m = (uint64_t)((u & 0x7fffffu) | 0x800000u);
-  int sh = ex - 150 + (int)kMassBits;  // p = m * 2^(ex - 150)
-  if (sh >= 0) return m << sh;         // sh <= 40 for p < 2
+  const uint64_t m = (uint64_t)((u & 0x7fffffu) | 0x800000u);
+  const int sh = ex - 150 + (int)kMassBits;  // p = m * 2^(ex - 150)
+  if (sh >= 0) return m << sh;               // sh <= 40 for p < 2
   if (sh <= -64) return 0;
   return m >> (-sh);
 }
 
 __device__ __forceinline__ float key_to_float(uint32_t key) {
-  uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
   return __uint_as_float(u);
 }
 
@@ -61,238 +60,413 @@ __device__ __forceinline__ bool is_forced(int c, const SelectArgs& a) {
   return (c >= a.t0 && c < a.t1) || (c >= a.e0 && c < a.e1);
 }
 
-template <int D, int MAXSLOTS>
-__global__ __launch_bounds__(256) void score_select_kernel(SelectArgs a) {
-  extern __shared__ float s_lds[];  // [kRowsPerWG][lds_stride]
-  const int bh = blockIdx.y;
-  const int row0 = blockIdx.x * kRowsPerWG;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nkb = a.nkb;
+// The threshold lies between the smallest and largest candidate key, so it shares their
+// common high bits: start from those bits and return the highest bit still to decide (-1 when
+// the two keys are equal).
+__device__ __forceinline__ int search_start(uint32_t kmin, uint32_t kmax, uint32_t* T) {
+  const uint32_t diff = kmin ^ kmax;
+  if (diff == 0) {
+    *T = kmin;
+    return -1;
+  }
+  const int hb = 31 - __builtin_clz(diff);
+  *T = hb == 31 ? 0u : (kmax & ~((2u << hb) - 1u));
+  return hb;
+}
 
-  // ---------------- phase 1: scores for 16 rows x all key blocks
-  {
-    constexpr int KSTEPS = D / 32;
-    const int m = lane & 15;       // A row / B column inside the 16x16 tile
-    const int kq = lane >> 4;      // which 8-wide k chunk of the 32
-    bf16x8 qhi[KSTEPS], qlo[KSTEPS];
-    {
-      const int qi = row0 + m;
-      const float* qrow = a.qbar + ((int64_t)bh * a.nqb + qi) * D;
+// Phase 0: wave w mean-pools query blocks row0 + 2 w and row0 + 2 w + 1 of this (batch, head)
+// straight from Q. A token row is kChunks 16-byte chunks; lane l sums chunk l % kChunks of
+// every (64 / kChunks)-th token of both blocks, with 16 loads in flight per lane (8 per block),
+// and the means are stored as bf16 hi | lo in qlds [16][2][D], the form the scoring MFMAs read.
+template <typename T, int D>
+__device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds, int bh, int row0,
+                                            int lane, int wave) {
+  constexpr int kVec = 16 / (int)sizeof(T);
+  constexpr int kChunks = D / kVec;
+  constexpr int kRowsPerLoad = 64 / kChunks;
+  constexpr int kLoads = kBlock / kRowsPerLoad;
+  constexpr int kBatch = 8;
+  static_assert(kLoads % kBatch == 0, "batching");
+  const int chunk = lane % kChunks;
+  const int r0 = lane / kChunks;
+  const int rr0 = 2 * wave;
+  const bool live0 = row0 + rr0 < a.nqb, live1 = row0 + rr0 + 1 < a.nqb;
+  if (!live0) return;
+  const T* src0 = static_cast<const T*>(a.q) + ((int64_t)bh * a.nqb + row0 + rr0) * kBlock * D +
+                  (int64_t)r0 * D + chunk * kVec;
+  // the second block is only read when it exists; otherwise the first is read twice
+  const T* src1 = live1 ? src0 + (int64_t)kBlock * D : src0;
+  float acc0[kVec], acc1[kVec];
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        float x[8];
-        if (qi < a.nqb) {
-          f32x4 v0 = *reinterpret_cast<const f32x4*>(qrow + ks * 32 + kq * 8);
-          f32x4 v1 = *reinterpret_cast<const f32x4*>(qrow + ks * 32 + kq * 8 + 4);
+  for (int e = 0; e < kVec; ++e) acc0[e] = acc1[e] = 0.f;
+  auto add = [](float* acc, const u32x4& raw) {
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { x[e] = v0[e]; x[4 + e] = v1[e]; }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
-        split_bf16(x, qhi[ks], qlo[ks]);
+      for (int w = 0; w < 4; ++w) {
+        acc[2 * w] += __uint_as_float(raw[w] << 16);
+        acc[2 * w + 1] += __uint_as_float(raw[w] & 0xffff0000u);
       }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc[w] += __uint_as_float(raw[w]);
     }
-    const int ntiles = (nkb + 15) >> 4;
-    const float* kbase = a.kbar + (int64_t)bh * nkb * D;
-    for (int t = wave; t < ntiles; t += 4) {
-      const int n = t * 16 + m;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  };
+#pragma unroll 1
+  for (int b = 0; b < kLoads; b += kBatch) {
+    u32x4 raw0[kBatch], raw1[kBatch];
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        float x[8];
-        if (n < nkb) {
-          const float* kr = kbase + (int64_t)n * D + ks * 32 + kq * 8;
-          f32x4 v0 = *reinterpret_cast<const f32x4*>(kr);
-          f32x4 v1 = *reinterpret_cast<const f32x4*>(kr + 4);
+    for (int i = 0; i < kBatch; ++i) {
+      const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
+      raw0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off));
+      raw1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off));
+    }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { x[e] = v0[e]; x[4 + e] = v1[e]; }
-        } else {
+    for (int i = 0; i < kBatch; ++i) {
+      add(acc0, raw0[i]);
+      add(acc1, raw1[i]);
+    }
+  }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
-        bf16x8 khi, klo;
-        split_bf16(x, khi, klo);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[ks], khi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[ks], klo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[ks], khi, acc, 0, 0, 0);
-      }
-      if (n < nkb) {
+  for (int off = kChunks; off < 64; off <<= 1)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_lds[(kq * 4 + r) * a.lds_stride + n] = acc[r] * a.scale;
+    for (int e = 0; e < kVec; ++e) {
+      acc0[e] += __shfl_xor(acc0[e], off, 64);
+      acc1[e] += __shfl_xor(acc1[e], off, 64);
+    }
+  if (lane < kChunks) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j == 1 && !live1) break;
+      const float* acc = j == 0 ? acc0 : acc1;
+      uint16_t* dst = qlds + (rr0 + j) * 2 * D + chunk * kVec;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float m = acc[e] * (1.0f / kBlock);
+        const uint32_t hi = f32_to_bf16_bits(m);
+        dst[e] = (uint16_t)hi;
+        dst[D + e] = (uint16_t)f32_to_bf16_bits(m - __uint_as_float(hi << 16));
       }
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void score_phase(const SelectArgs& a, float* s_lds,
+                                            const uint16_t* qlds, int bh, int row0, int lane,
+                                            int wave) {
+  constexpr int KSTEPS = D / 32;
+  const int nkb = a.nkb;
+  const int m = lane & 15;   // A row / B column inside the 16x16 tile
+  const int kq = lane >> 4;  // which 8-wide k chunk of the 32
+  bf16x8 qhi[KSTEPS], qlo[KSTEPS];
+  {
+    const bool live = row0 + m < a.nqb;
+    const uint16_t* qrow = qlds + m * 2 * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      qhi[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + kq * 8);
+      qlo[ks] = *reinterpret_cast<const bf16x8*>(qrow + D + ks * 32 + kq * 8);
+      if (!live) {
+        qhi[ks] = bf16x8{};
+        qlo[ks] = bf16x8{};
+      }
+    }
+  }
+  const int ntiles = (nkb + 15) >> 4;
+  // tiled operand order written by the pooling kernel: [tile][ks][hi | lo][64 lanes][8]
+  const uint16_t* kbase = a.ksplit + (int64_t)bh * ntiles * KSTEPS * 2 * 512 + lane * 8;
+  bf16x8 khi[KSTEPS], klo[KSTEPS];
+  auto load_tile = [&](int t) {
+    const uint16_t* kr = kbase + (int64_t)t * KSTEPS * 2 * 512;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      khi[ks] = *reinterpret_cast<const bf16x8*>(kr + (2 * ks) * 512);
+      klo[ks] = *reinterpret_cast<const bf16x8*>(kr + (2 * ks + 1) * 512);
+    }
+  };
+  int t = wave;
+  if (t < ntiles) load_tile(t);
+  for (; t < ntiles; t += kWaves) {
+    bf16x8 chi[KSTEPS], clo[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      chi[ks] = khi[ks];
+      clo[ks] = klo[ks];
+    }
+    if (t + kWaves < ntiles) load_tile(t + kWaves);  // next tile in flight during the MFMAs
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[ks], chi[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[ks], clo[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[ks], chi[ks], acc, 0, 0, 0);
+    }
+    const int n = t * 16 + m;
+    if (n < nkb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_lds[(kq * 4 + r) * a.lds_stride + n] = acc[r] * a.scale;
+    }
+  }
+}
+
+// Radix step of the Top-K threshold search. Among the candidate keys that share the already
+// decided high bits `prefix` (bits above shift + 8), count them per 8-bit digit at bits
+// [shift, shift + 8) in the wave's LDS histogram, then find the largest digit d for which at
+// least `need` keys have digit >= d. Returns d and, via *above, how many keys have a larger
+// digit and, via *bucket, how many have digit d. `hist` is this wave's 256-entry histogram;
+// all calls are wave-uniform.
+template <int S>
+__device__ __forceinline__ int radix_digit(const uint32_t (&key)[S], uint32_t prefix, int shift,
+                                           uint32_t need, uint32_t* hist, int lane,
+                                           uint32_t* above, uint32_t* bucket) {
+  *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+  __builtin_amdgcn_wave_barrier();
+  const int hs = shift + 8;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const uint32_t k = key[e];
+    const bool in = k != 0u && (hs >= 32 || (k >> hs) == (prefix >> hs));
+    if (in) __hip_atomic_fetch_add(hist + ((k >> shift) & 0xffu), 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane l reads the four digits 4 (63 - l) .. 4 (63 - l) + 3, so lanes run from the highest
+  // digits down and an inclusive prefix sum over lanes counts keys with digit >= 4 (63 - l)
+  const int g = 63 - lane;
+  const u32x4 b = *reinterpret_cast<const u32x4*>(hist + 4 * g);
+  const uint32_t t = b[0] + b[1] + b[2] + b[3];
+  const uint32_t suf = wave_prefix_sum_u32(t);
+  const uint32_t hi = suf - t;  // keys with a digit above 4 g + 3
+  const bool here = hi < need && suf >= need;
+  const uint64_t m = ballot64(here);
+  const int src = (int)__builtin_ctzll(m);  // exactly one lane holds the crossing digit
+  int d;
+  uint32_t a, n;
+  if (hi + b[3] >= need) { d = 3; a = hi; n = b[3]; }
+  else if (hi + b[3] + b[2] >= need) { d = 2; a = hi + b[3]; n = b[2]; }
+  else if (hi + b[3] + b[2] + b[1] >= need) { d = 1; a = hi + b[3] + b[2]; n = b[1]; }
+  else { d = 0; a = hi + b[3] + b[2] + b[1]; n = b[0]; }
+  d = (int)lane_u32((uint32_t)(4 * g + d), src);
+  *above = lane_u32(a, src);
+  *bucket = lane_u32(n, src);
+  return d;
+}
+
+// Top-K selection of one row held as S slots per lane; writes col_idx and (lane 0) row_ptr.
+// The K-th largest candidate key T is found one byte at a time, most significant first
+// (radix select); a byte whose bucket holds exactly the remaining count ends the search early.
+// All ballots and shuffles sit in wave-uniform control flow.
+template <int S>
+__device__ __forceinline__ void select_topk_row(const SelectArgs& a, const float* srow,
+                                                int64_t row, int lane, uint32_t* hist) {
+  const int nkb = a.nkb;
+  float val[S];
+  uint32_t key[S];
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    const bool valid = c < nkb;
+    val[e] = valid ? srow[c] : 0.f;
+    key[e] = (valid && !is_forced(c, a)) ? order_key(val[e]) : 0u;  // 0: not a candidate
+  }
+  if (a.scores_out) {
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+      const int c = e * 64 + lane;
+      if (c < nkb) a.scores_out[row * nkb + c] = val[e];
+    }
+  }
+  const uint32_t kk = (uint32_t)a.kk;
+  uint32_t T = 0;     // threshold key (its decided high bytes)
+  uint32_t need = kk; // candidates still to take among keys matching T's decided bytes
+  bool exact = true;  // true: keep exactly the candidate keys whose decided bytes >= T's
+  int low = 0;        // bits of T below this are undecided (exact) or zero (tie case)
+  if (kk > 0) {
+    exact = false;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      uint32_t above, cnt_d;
+      const int d = radix_digit<S>(key, T, shift, need, hist, lane, &above, &cnt_d);
+      T |= (uint32_t)d << shift;
+      need -= above;
+      low = shift;
+      if (cnt_d == need) {  // the whole bucket is taken
+        exact = true;
+        break;
+      }
+    }
+  }
+  // exact: keep keys whose bits >= low compare >= T's; otherwise keep keys > T and the first
+  // `need` keys equal to T in ascending block order.
+  int64_t out = row * (int64_t)a.per_row;
+  uint32_t eq_seen = 0;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    const bool valid = c < nkb;
+    const bool candidate = key[e] != 0u && kk > 0;
+    const uint32_t kh = low >= 32 ? 0u : (key[e] >> low);
+    const uint32_t th = low >= 32 ? 0u : (T >> low);
+    const bool eq = candidate && !exact && key[e] == T;
+    const uint64_t eqm = ballot64(eq);
+    const bool take = candidate && (exact ? kh >= th
+                                          : (key[e] > T || (eq && eq_seen + (uint32_t)mbcnt64(eqm) < need)));
+    eq_seen += (uint32_t)__popcll(eqm);
+    const bool keep = (valid && is_forced(c, a)) || take;
+    const uint64_t km = ballot64(keep);
+    const int64_t pos = out + mbcnt64(km);
+    if (keep && pos < a.col_capacity) a.col_idx[pos] = c;
+    out += __popcll(km);
+  }
+  if (lane == 0) {
+    a.row_ptr[row] = (int32_t)(row * a.per_row);
+    if (row == (int64_t)a.n_rows - 1) a.row_ptr[row + 1] = (int32_t)((row + 1) * a.per_row);
+  }
+}
+
+// Cumulative-mass selection of one row; writes the kept bitmask words and count.
+template <int S>
+__device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float* srow,
+                                                int64_t row, int lane) {
+  const int nkb = a.nkb;
+  float val[S];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    val[e] = c < nkb ? srow[c] : -INFINITY;
+    mx = fmaxf(mx, val[e]);
+  }
+  mx = wave_max_dpp(mx);
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    val[e] = c < nkb ? __expf(val[e] - mx) : 0.f;
+    part += val[e];
+  }
+  const float inv = 1.0f / wave_total_f32(part);
+  uint64_t u[S];
+  uint32_t key[S];
+  uint64_t fsum = 0, csum = 0;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    const bool valid = c < nkb;
+    const float p = val[e] * inv;
+    if (valid && a.scores_out) a.scores_out[row * nkb + c] = p;
+    const bool f = valid && is_forced(c, a);
+    u[e] = valid ? mass_units(p) : 0ull;
+    key[e] = (valid && !f) ? order_key(p) : 0u;
+    if (f) fsum += u[e];
+    else csum += u[e];
+    if (key[e] != 0u) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
+  }
+  fsum = wave_total_u64(fsum);
+  csum = wave_total_u64(csum);
+  // how: 0 keep forced only, 1 keep all, 2 threshold
+  int how;
+  uint64_t need_mass = 0;
+  if (a.keep_all) {
+    how = 1;
+  } else if (fsum >= a.theta) {
+    how = 0;
+  } else {
+    need_mass = a.theta - fsum;
+    how = (csum < need_mass) ? 1 : 2;
+  }
+  uint32_t T = 0;
+  uint64_t n_eq = 0;
+  if (how == 2) {
+    kmin = wave_min_dpp(kmin);
+    kmax = wave_max_u32_dpp(kmax);
+    // invariant: the candidate keys >= T carry at least need_mass (T <= kmin at the start)
+    int bit = search_start(kmin, kmax, &T);
+    for (; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      uint64_t s = 0;
+#pragma unroll
+      for (int e = 0; e < S; ++e) s += key[e] >= cand ? u[e] : 0ull;
+      s = wave_total_u64(s);
+      if (s >= need_mass) T = cand;
+    }
+    uint64_t above = 0;
+#pragma unroll
+    for (int e = 0; e < S; ++e) above += key[e] > T ? u[e] : 0ull;
+    above = wave_total_u64(above);
+    // T is the key of a candidate whose mass completes the prefix, so uT > 0
+    const uint64_t uT = mass_units(key_to_float(T));
+    n_eq = (need_mass - above + uT - 1) / uT;
+  }
+  uint32_t cnt = 0;
+  uint64_t eq_seen = 0;
+  uint64_t* mrow = a.masks + row * a.words;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    const bool valid = c < nkb;
+    const bool eq = how == 2 && key[e] != 0u && key[e] == T;
+    const uint64_t eqm = ballot64(eq);
+    bool keep;
+    if (how == 1) {
+      keep = valid;
+    } else {
+      keep = valid && is_forced(c, a);
+      if (how == 2)
+        keep = keep || (key[e] != 0u && key[e] > T) ||
+               (eq && eq_seen + (uint64_t)mbcnt64(eqm) < n_eq);
+    }
+    eq_seen += (uint64_t)__popcll(eqm);
+    const uint64_t km = ballot64(keep);
+    if (lane == 0 && e < a.words) mrow[e] = km;
+    cnt += (uint32_t)__popcll(km);
+  }
+  if (lane == 0) a.counts[row] = (int32_t)cnt;
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin by id, so id b runs on XCD b % 8. Work item
+// w = (head, row tile) is assigned as w = (b % 8) * per_xcd + b / 8: each XCD walks a contiguous
+// range of work items, i.e. whole heads one after another, and keeps the pooled keys of the
+// head it is on (2 * nkb * head_dim * 2 bytes) in its own L2.
+__device__ __forceinline__ bool xcd_work_item(int64_t n_items, int64_t* item) {
+  const int64_t per_xcd = (n_items + 7) / 8;
+  const int64_t b = blockIdx.x;
+  *item = (b % 8) * per_xcd + b / 8;
+  return *item < n_items;
+}
+
+template <typename T, int D, int S, int MODE>
+__global__ __launch_bounds__(64 * kWaves) void score_select_kernel(SelectArgs a, int n_heads) {
+  // [kRowsPerWG][lds_stride] scores, then an 8 KiB area holding first the pooled queries
+  // (phases 0-1) and then one 256-bin histogram per wave (phase 2, Top-K)
+  extern __shared__ float s_lds[];
+  const int tiles = (a.nqb + kRowsPerWG - 1) / kRowsPerWG;
+  int64_t item;
+  if (!xcd_work_item((int64_t)n_heads * tiles, &item)) return;
+  const int bh = (int)(item / tiles);
+  const int row0 = (int)(item - (int64_t)bh * tiles) * kRowsPerWG;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+
+  uint16_t* qlds = reinterpret_cast<uint16_t*>(s_lds + kRowsPerWG * a.lds_stride);
+  pool_q_rows<T, D>(a, qlds, bh, row0, lane, wave);
+  __syncthreads();
+  score_phase<D>(a, s_lds, qlds, bh, row0, lane, wave);
   __syncthreads();
 
-  // ---------------- phase 2: per-row selection, one wave per row
-  const int slots = (nkb + 63) >> 6;
-  for (int rr = wave; rr < kRowsPerWG; rr += 4) {
+  for (int rr = wave; rr < kRowsPerWG; rr += kWaves) {
     const int qi = row0 + rr;
     if (qi >= a.nqb) break;
     const int64_t row = (int64_t)bh * a.nqb + qi;
     const float* srow = s_lds + rr * a.lds_stride;
-
-    float val[MAXSLOTS];
-    uint32_t key[MAXSLOTS];
-#pragma unroll
-    for (int e = 0; e < MAXSLOTS; ++e) {
-      const int c = e * 64 + lane;
-      val[e] = (e < slots && c < nkb) ? srow[c] : 0.f;
-    }
-
-    if (a.mode == 0) {
-      // ---- Top-K
-      if (a.scores_out) {
-#pragma unroll
-        for (int e = 0; e < MAXSLOTS; ++e) {
-          const int c = e * 64 + lane;
-          if (e < slots && c < nkb) a.scores_out[row * nkb + c] = val[e];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < MAXSLOTS; ++e) {
-        const int c = e * 64 + lane;
-        key[e] = (e < slots && c < nkb && !is_forced(c, a)) ? order_key(val[e]) : 0u;
-      }
-      const uint32_t kk = (uint32_t)a.kk;
-      uint32_t T = 0;
-      bool exact = false;
-      if (kk > 0) {
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = T | (1u << bit);
-          uint32_t cnt = 0;
-#pragma unroll
-          for (int e = 0; e < MAXSLOTS; ++e)
-            if (e < slots) cnt += (uint32_t)__popcll(ballot64(key[e] >= cand));
-          if (cnt >= kk) {
-            T = cand;
-            if (cnt == kk) { exact = true; break; }
-          }
-        }
-      }
-      uint32_t need = 0;  // how many keys equal to T are kept
-      if (kk > 0 && !exact) {
-        uint32_t gt = 0;
-#pragma unroll
-        for (int e = 0; e < MAXSLOTS; ++e)
-          if (e < slots) gt += (uint32_t)__popcll(ballot64(key[e] > T));
-        need = kk - gt;
-      }
-      int64_t out = row * (int64_t)a.per_row;
-      uint32_t eq_seen = 0;
-#pragma unroll
-      for (int e = 0; e < MAXSLOTS; ++e) {
-        if (e >= slots) continue;
-        const int c = e * 64 + lane;
-        const bool valid = c < nkb;
-        bool keep = valid && is_forced(c, a);
-        if (kk > 0) {
-          if (exact) {
-            keep = keep || key[e] >= T;
-          } else {
-            const bool eq = key[e] == T;
-            const uint64_t eqm = ballot64(eq);
-            keep = keep || key[e] > T || (eq && eq_seen + (uint32_t)mbcnt64(eqm) < need);
-            eq_seen += (uint32_t)__popcll(eqm);
-          }
-        }
-        const uint64_t km = ballot64(keep);
-        const int64_t pos = out + mbcnt64(km);
-        if (keep && pos < a.col_capacity) a.col_idx[pos] = c;
-        out += __popcll(km);
-      }
-      if (lane == 0) {
-        a.row_ptr[row] = (int32_t)(row * a.per_row);
-        if (row == (int64_t)gridDim.y * a.nqb - 1) a.row_ptr[row + 1] = (int32_t)((row + 1) * a.per_row);
-      }
-    } else {
-      // ---- cumulative mass over the softmax of the row
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < MAXSLOTS; ++e) {
-        const int c = e * 64 + lane;
-        if (e < slots && c < nkb) mx = fmaxf(mx, val[e]);
-      }
-      mx = wave_max_f32(mx);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < MAXSLOTS; ++e) {
-        const int c = e * 64 + lane;
-        val[e] = (e < slots && c < nkb) ? __expf(val[e] - mx) : 0.f;
-        part += val[e];
-      }
-      const float inv = 1.0f / wave_sum_f32(part);
-      uint64_t fsum = 0, csum = 0;
-#pragma unroll
-      for (int e = 0; e < MAXSLOTS; ++e) {
-        const int c = e * 64 + lane;
-        const bool valid = e < slots && c < nkb;
-        const float p = val[e] * inv;
-        val[e] = p;
-        if (valid && a.scores_out) a.scores_out[row * nkb + c] = p;
-        const bool f = valid && is_forced(c, a);
-        key[e] = (valid && !f) ? order_key(p) : 0u;
-        const uint64_t u = valid ? mass_units(p) : 0ull;
-        if (f) fsum += u; else csum += u;
-      }
-      fsum = wave_sum_u64(fsum);
-      csum = wave_sum_u64(csum);
-      // mode: 0 keep forced only, 1 keep all, 2 threshold
-      int how;
-      uint64_t need_mass = 0;
-      if (a.keep_all) how = 1;
-      else if (fsum >= a.theta) how = 0;
-      else {
-        need_mass = a.theta - fsum;
-        how = (csum < need_mass) ? 1 : 2;
-      }
-      uint32_t T = 0;
-      uint64_t n_eq = 0;
-      if (how == 2) {
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = T | (1u << bit);
-          uint64_t s = 0;
-#pragma unroll
-          for (int e = 0; e < MAXSLOTS; ++e)
-            if (e < slots && key[e] >= cand) s += mass_units(val[e]);
-          s = wave_sum_u64(s);
-          if (s >= need_mass) T = cand;
-        }
-        uint64_t above = 0;
-#pragma unroll
-        for (int e = 0; e < MAXSLOTS; ++e)
-          if (e < slots && key[e] > T) above += mass_units(val[e]);
-        above = wave_sum_u64(above);
-        const uint64_t uT = mass_units(key_to_float(T));  // > 0 by construction of T
-        n_eq = (need_mass - above + uT - 1) / uT;
-      }
-      uint32_t cnt = 0;
-      uint64_t eq_seen = 0;
-      uint64_t* mrow = a.masks + row * a.words;
-#pragma unroll
-      for (int e = 0; e < MAXSLOTS; ++e) {
-        if (e >= slots) continue;
-        const int c = e * 64 + lane;
-        const bool valid = c < nkb;
-        bool keep;
-        if (how == 1) keep = valid;
-        else {
-          keep = valid && is_forced(c, a);
-          if (how == 2) {
-            const bool eq = key[e] == T;
-            const uint64_t eqm = ballot64(eq);
-            keep = keep || key[e] > T || (eq && eq_seen + (uint64_t)mbcnt64(eqm) < n_eq);
-            eq_seen += (uint64_t)__popcll(eqm);
-          }
-        }
-        const uint64_t km = ballot64(keep);
-        if (lane == 0) mrow[e] = km;
-        cnt += (uint32_t)__popcll(km);
-      }
-      if (lane == 0) a.counts[row] = (int32_t)cnt;
-    }
+    if (MODE == 0)
+      select_topk_row<S>(a, srow, row, lane,
+                         reinterpret_cast<uint32_t*>(s_lds + kRowsPerWG * a.lds_stride) + 256 * wave);
+    else
+      select_mass_row<S>(a, srow, row, lane);
   }
 }
 
@@ -342,27 +516,41 @@ __global__ __launch_bounds__(256) void fill_csr_kernel(const uint64_t* __restric
   }
 }
 
-template <int D>
-static hipError_t launch_score_select_d(const SelectArgs& a, int64_t bh, hipStream_t stream) {
-  dim3 grid((unsigned)((a.nqb + kRowsPerWG - 1) / kRowsPerWG), (unsigned)bh), block(256);
-  size_t lds = (size_t)kRowsPerWG * a.lds_stride * sizeof(float);
+template <typename T, int D, int MODE>
+static hipError_t launch_score_select_dm(const SelectArgs& a, int64_t bh, hipStream_t stream) {
+  const int64_t items = bh * ((a.nqb + kRowsPerWG - 1) / kRowsPerWG);
+  const dim3 grid((unsigned)(8 * ((items + 7) / 8)));
+  const dim3 block(64 * kWaves);
+  const size_t lds = (size_t)kRowsPerWG * a.lds_stride * sizeof(float) + 8192;
   const int slots = (a.nkb + 63) / 64;
-  if (slots <= 4)
-    score_select_kernel<D, 4><<<grid, block, lds, stream>>>(a);
-  else if (slots <= 8)
-    score_select_kernel<D, 8><<<grid, block, lds, stream>>>(a);
-  else if (slots <= 16)
-    score_select_kernel<D, 16><<<grid, block, lds, stream>>>(a);
-  else
-    score_select_kernel<D, 32><<<grid, block, lds, stream>>>(a);
-  return hipGetLastError();
+#define DBSP_SLOTS(N)                                                               \
+  if (slots <= N) {                                                                 \
+    score_select_kernel<T, D, N, MODE><<<grid, block, lds, stream>>>(a, (int)bh);               \
+    return hipGetLastError();                                                       \
+  }
+  DBSP_SLOTS(1) DBSP_SLOTS(2) DBSP_SLOTS(4) DBSP_SLOTS(6) DBSP_SLOTS(8) DBSP_SLOTS(10)
+  DBSP_SLOTS(12) DBSP_SLOTS(16) DBSP_SLOTS(20) DBSP_SLOTS(24) DBSP_SLOTS(28) DBSP_SLOTS(32)
+#undef DBSP_SLOTS
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, hipStream_t stream) {
+hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, bool bf16,
+                         hipStream_t stream) {
   hipError_t err;
-  if (head_dim == 128) err = launch_score_select_d<128>(a, bh, stream);
-  else if (head_dim == 64) err = launch_score_select_d<64>(a, bh, stream);
-  else return hipErrorInvalidValue;
+  if (bf16 && head_dim == 128)
+    err = a.mode == 0 ? launch_score_select_dm<uint16_t, 128, 0>(a, bh, stream)
+                      : launch_score_select_dm<uint16_t, 128, 1>(a, bh, stream);
+  else if (bf16 && head_dim == 64)
+    err = a.mode == 0 ? launch_score_select_dm<uint16_t, 64, 0>(a, bh, stream)
+                      : launch_score_select_dm<uint16_t, 64, 1>(a, bh, stream);
+  else if (!bf16 && head_dim == 128)
+    err = a.mode == 0 ? launch_score_select_dm<float, 128, 0>(a, bh, stream)
+                      : launch_score_select_dm<float, 128, 1>(a, bh, stream);
+  else if (!bf16 && head_dim == 64)
+    err = a.mode == 0 ? launch_score_select_dm<float, 64, 0>(a, bh, stream)
+                      : launch_score_select_dm<float, 64, 1>(a, bh, stream);
+  else
+    return hipErrorInvalidValue;
   if (err != hipSuccess || a.mode == 0) return err;
   const int64_t rows = bh * a.nqb;
   scan_counts_kernel<<<1, 1024, 0, stream>>>(a.counts, a.row_ptr, rows);

@@ -114,8 +114,9 @@ def test_mass_bound_and_workspace(lib):
     ws_topk, ws_mass = ctypes.c_uint64(), ctypes.c_uint64()
     assert lib.dbsp_select_workspace_bytes(ctypes.byref(dims), _abi.DBSP_TOPK, ctypes.byref(ws_topk)) == 0
     assert lib.dbsp_select_workspace_bytes(ctypes.byref(dims), _abi.DBSP_MASS, ctypes.byref(ws_mass)) == 0
-    pooled = (w.rows + w.batch * w.heads * w.n_k_blocks) * w.head_dim * 4
-    assert ws_topk.value >= pooled and ws_mass.value > ws_topk.value
+    # pooled keys (bf16 hi and lo halves, tiles of 16 key blocks); pooled queries stay on chip
+    pooled_keys = w.batch * w.heads * (-(-w.n_k_blocks // 16) * 16) * w.head_dim * 4
+    assert ws_topk.value >= pooled_keys and ws_mass.value > ws_topk.value
 
 
 def _select(lib, dims, mode=_abi.DBSP_TOPK, param=0.5, text=(0, 1), extra=(0, 0), q=FAKE, k=FAKE,
