@@ -71,18 +71,28 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
   return d;
 }
 
-// Issue the DMA of one 128 x 128 bf16 tile (32 KiB at `tile`, wave-uniform) into LDS: wave w
-// copies rows 32 w .. 32 w + 31, one 4-row slab (1 KiB) per instruction, lane l landing at byte
-// 16 l of the slab, so the swizzle is applied on the global side.
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor: 32-bit data format, no
+// stride, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Issue the DMA of one 128 x 128 bf16 tile (32 KiB at byte `tile_off` of the head's K or V,
+// wave-uniform) into LDS: wave w copies rows 32 w .. 32 w + 31, one 4-row slab (1 KiB) per
+// instruction, lane l landing at byte 16 l of the slab, so the swizzle is applied on the global
+// side. The buffer form takes the tile offset in a scalar register and the lane offset in a
+// 32-bit vector register, so the addressing costs no vector instructions.
 template <bool kIsV>
-__device__ __forceinline__ void tile_dma(const char* tile, uint16_t* lds, int w,
-                                         const DmaOffsets& d) {
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t src, int tile_off, uint16_t* lds,
+                                         int w, const DmaOffsets& d) {
+  const int wave_off = tile_off + w * (32 * 256);
+  uint16_t* wave_dst = lds + w * (32 * 128);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int slab = 32 * w + 4 * i;  // first row of the slab
-    const char* src = tile + slab * 256 + (kIsV ? d.v : d.k[i & 3]);
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + slab * 128), 16, 0, 0);
-  }
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(wave_dst + 4 * i * 128), 16,
+                                             kIsV ? d.v : d.k[i & 3], wave_off + 4 * i * 256, 0,
+                                             0);
 }
 
 __device__ __forceinline__ int64_t clip64(int64_t x, int64_t lo, int64_t hi) {
@@ -137,16 +147,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int qb = (int)(row - bh * nqb);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int64_t lq = (int64_t)nqb * kBlock;
   const int64_t lk = (int64_t)nkb * kBlock;
 
-  const char* kp = reinterpret_cast<const char*>(kg + bh * lk * 128);
-  const char* vp = reinterpret_cast<const char*>(vg + bh * lk * 128);
+  // K and V of this (batch, head): lk x 128 bf16 each, at most 2048 blocks of 32 KiB
+  const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kg + bh * lk * 128, (uint32_t)(lk * 256));
+  const __amdgpu_buffer_rsrc_t vbuf = raw_buffer(vg + bh * lk * 128, (uint32_t)(lk * 256));
   const DmaOffsets dmo = dma_offsets(lane);
-  constexpr int64_t kTileBytes = (int64_t)kBlock * 128 * 2;
+  constexpr int kTileBytes = kBlock * 128 * 2;
 
   // Q^T as the B operand of S^T = K Q^T: lane (h, l32) holds query 32 w + l32, dims 16 s + 8 h .. +7
   const int64_t qtok = bh * lq + (int64_t)qb * kBlock + 32 * w + l32;
@@ -176,8 +187,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     if (n == 0) continue;
     {
       const int cb = __builtin_amdgcn_readfirstlane(list[0]);
-      tile_dma<false>(kp + cb * kTileBytes, k_lds, w, dmo);
-      tile_dma<true>(vp + cb * kTileBytes, v_lds, w, dmo);
+      tile_dma<false>(kbuf, cb * kTileBytes, k_lds, w, dmo);
+      tile_dma<true>(vbuf, cb * kTileBytes, v_lds, w, dmo);
     }
     for (int i = 0; i < n; ++i) {
       const bool more = i + 1 < n;
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       const int cb_next = __builtin_amdgcn_readfirstlane(list[more ? i + 1 : i]);
       wait_lgkmcnt0();
       wg_barrier();  // every wave is done reading K(i)
-      tile_dma<false>(kp + cb_next * kTileBytes, k_lds, w, dmo);
+      tile_dma<false>(kbuf, cb_next * kTileBytes, k_lds, w, dmo);
 
       // online softmax for query column l32 (lanes l32 and l32 + 32 share it), exp2 domain
       float mx = -INFINITY;
@@ -248,8 +259,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
           const int col = 32 * nt + tr_col;
           const int off_lo = jb * 128 + v_swz(jb, col >> 3) * 8 + (col & 7);
           const int off_hi = (jb + 8) * 128 + v_swz(jb + 8, col >> 3) * 8 + (col & 7);
-          // whole-vector casts only: an element-wise rebuild of these results has been seen to
-          // lose the upper dword of each read in the generated code
+          // whole-vector casts only: __builtin_bit_cast of a vector element reads element 0
+          // whatever the index with this compiler, which loses the upper dword of each read
           const u32x2 lo = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_lo)));
           const u32x2 hi = __builtin_bit_cast(
@@ -261,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       }
       wait_lgkmcnt0();
       wg_barrier();  // every wave is done reading V(i)
-      tile_dma<true>(vp + cb_next * kTileBytes, v_lds, w, dmo);
+      tile_dma<true>(vbuf, cb_next * kTileBytes, v_lds, w, dmo);
     }
     wait_vmcnt<0>();
   }
