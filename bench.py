@@ -10,11 +10,25 @@ density 0.09375). Prints one JSON line.
 
 Reported numbers:
   value           executed attention FLOP of the step / step time (TFLOP/s)
-  select_ms       per-step time of the selection kernels (HIP events on the launch stream)
+  select_ms       per-step time of the selection kernels (HIP events on the launch stream), mean
+                  of the timed steps; select_ms_p10/p50/p90 give the spread
   select_GBps     selection's algorithmic bytes (Q + K read once, CSR written) / select_ms
-  attn_ms         per-step time of the attention kernel (HIP events on the launch stream)
+  attn_ms         per-step time of the attention kernel (HIP events on the launch stream), mean;
+                  attn_ms_p10/p50/p90 give the spread
+  attn_kv_GBps    attention's algorithmic bytes (Q and O once, K and V of every kept block once
+                  per query block) / attn_ms, and attn_kv_hbm_frac against 8 TB/s: the executed
+                  FLOP per such byte is 2 x 128 = 256 / 2 = 128 for 128-token blocks, below the
+                  chip's FLOP-per-byte ridge, so without reuse across query blocks in the caches
+                  the HBM side bounds the kernel before the MFMA side does
+  cold            the same two calls timed after overwriting a 512 MiB scratch buffer before
+                  every iteration (outside the timed region), which evicts the 256 MiB
+                  last-level cache: medians over the cold iterations
+  copy_GBps       a plain device-to-device copy of 1 GiB (read + write bytes / time) as the
+                  achievable HBM ceiling, with select_copy_frac = select_GBps / copy_GBps
   roofline        the attention kernel (dominant): executed FLOP / its average launch time,
-                  against the bf16 dense MFMA peak
+                  against the bf16 dense MFMA peak; traffic = its HBM bytes per launch from the
+                  committed FETCH_SIZE / WRITE_SIZE counter summary, when that summary was
+                  taken on the current kernel source (else null)
   cpu_baseline    the float64 NumPy oracle on the host cores, on a bounded sample of the same
                   workload, extrapolated to the whole step in the same unit
 """
@@ -32,6 +46,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn fwd ms + MFMA util @72k-token scale; select ms + HBM GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_final_720p.json")
+ATTN_SOURCES = ("attn.hip", "common.hpp", "kernels.hpp")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
@@ -46,7 +62,59 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
+    ap.add_argument("--only-copy", action="store_true",
+                    help="run only the 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--cold-iters", type=int, default=8,
+                    help="iterations of the cache-flushed timing pass (0 skips it)")
     return ap.parse_args()
+
+
+def attn_source_hash() -> str:
+    """sha256 over the attention kernel's sources, to tell whether a stored counter summary
+    still describes the kernel that runs."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "dynamic_block_sparse_pool_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, or None when it is
+    missing, for another workload, or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != attn_source_hash():
+        return None
+    return int(t["traffic_bytes"])
+
+
+def percentiles(xs):
+    ys = sorted(xs)
+    pick = lambda f: ys[min(len(ys) - 1, max(0, int(round(f * (len(ys) - 1)))))]
+    return pick(0.1), pick(0.5), pick(0.9)
+
+
+def copy_ceiling(torch, dev, reps: int = 5) -> float:
+    """Read + write GB/s of a plain 1 GiB device-to-device copy."""
+    n = 1 << 28  # float32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(w, q, k, v, row_ptr, col_idx, nnz, flop_per_pair, budget_s):
@@ -109,6 +177,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.only_copy:
+        torch.cuda.set_device(0)
+        print(json.dumps({"copy_GBps": round(copy_ceiling(torch, torch.device("cuda:0")), 1)}))
+        return
     import dynamic_block_sparse_pool_amd as dbsp
     from synth import BENCH_WORKLOAD, WORKLOADS, make_qkv
 
@@ -146,9 +218,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    sel_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / n_ev
-    att_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / n_ev
+    sel_list = [e[0].elapsed_time(e[1]) for e in ev]
+    att_list = [e[1].elapsed_time(e[2]) for e in ev]
+    sel_ms = sum(sel_list) / n_ev
+    att_ms = sum(att_list) / n_ev
     ms_per_step = wall * 1e3 / args.steps
+
+    # cold pass: evict the last-level cache before every iteration, outside the timed region
+    cold = None
+    if args.cold_iters > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cs, ca = [], []
+        for it in range(args.cold_iters):
+            scratch.fill_(it & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(e)
+            torch.cuda.synchronize()
+            cs.append(e[0].elapsed_time(e[1]))
+            ca.append(e[1].elapsed_time(e[2]))
+        del scratch
+        cold = {"iters": args.cold_iters, "flush_bytes": 512 << 20,
+                "select_ms_p50": round(percentiles(cs)[1], 4),
+                "attn_ms_p50": round(percentiles(ca)[1], 4)}
+    copy_gbps = copy_ceiling(torch, dev)
 
     nnz = idx.nnz()
     rows = w.rows
@@ -158,6 +250,14 @@ def main():
     sel_bytes = (w.batch * w.heads * (w.lq + w.lk) * w.head_dim * elt) + 4 * (rows + 1) + 4 * nnz
     att_tflops = exec_flop / (att_ms * 1e-3) / 1e12
     sel_gbps = sel_bytes / (sel_ms * 1e-3) / 1e9
+    tok_bytes = 128 * w.head_dim * elt  # one block of K or V
+    att_bytes = nnz * 2 * tok_bytes + 2 * w.batch * w.heads * w.lq * w.head_dim * elt
+    att_gbps = att_bytes / (att_ms * 1e-3) / 1e9
+    if cold is not None:
+        cold["select_GBps"] = round(sel_bytes / (cold["select_ms_p50"] * 1e-3) / 1e9, 1)
+        cold["attn_TFLOPs"] = round(exec_flop / (cold["attn_ms_p50"] * 1e-3) / 1e12, 2)
+    sp, ap_ = percentiles(sel_list), percentiles(att_list)
+    traffic = stored_traffic(w.name)
     res = {
         "metric": METRIC,
         "value": round(exec_flop / (ms_per_step * 1e-3) / 1e12, 3),
@@ -179,14 +279,23 @@ def main():
             "output_dtype": "bf16",
         },
         "select_ms": round(sel_ms, 4),
+        "select_ms_p10": round(sp[0], 4), "select_ms_p50": round(sp[1], 4),
+        "select_ms_p90": round(sp[2], 4),
         "select_GBps": round(sel_gbps, 1),
         "select_hbm_frac": round(sel_gbps / PEAK_HBM_GBPS, 4),
+        "copy_GBps": round(copy_gbps, 1),
+        "select_copy_frac": round(sel_gbps / copy_gbps, 4),
         "attn_ms": round(att_ms, 4),
+        "attn_ms_p10": round(ap_[0], 4), "attn_ms_p50": round(ap_[1], 4),
+        "attn_ms_p90": round(ap_[2], 4),
         "attn_TFLOPs": round(att_tflops, 2),
         "attn_mfma_frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_kv_GBps": round(att_gbps, 1),
+        "attn_kv_hbm_frac": round(att_gbps / PEAK_HBM_GBPS, 4),
+        "cold": cold,
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fwd_bf16_kernel",
+                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel",
                      "per_launch_flop": exec_flop},
     }
     if not args.no_cpu_baseline:

@@ -7,11 +7,12 @@
 //
 // attn_fwd_bf16_kernel (bf16, head_dim 128): one workgroup of 4 waves per CSR row (one query
 // block of 128 tokens); wave w owns queries [32 w, 32 w + 32). Per kept key block:
-//   * K [128 x 128] and V [128 x 128] are copied to LDS (rows padded against bank conflicts);
+//   * K [128 x 128] and V [128 x 128] are copied to LDS (XOR-swizzled against bank conflicts);
 //   * S^T = K Q^T on 32x32x16 bf16 MFMAs: Q^T is the B operand, held in registers for the
 //     whole row; the result leaves every lane with one query column and 64 key rows, so the
 //     row max needs one cross-half exchange;
-//   * an fp32 online softmax in the exp2 domain (the log2(e) factor folded into the scale);
+//   * an fp32 online softmax in the exp2 domain (the log2(e) factor folded into the scale)
+//     whose exponent reference is raised lazily, only when a block exceeds it by 2^8;
 //   * O^T += V^T P^T: the probabilities go straight from the S^T accumulators (as bf16) into
 //     the B operand, and V^T comes from LDS through ds_read_tr16_b64, which transposes 4x16-bit
 //     groups across each 16-lane block on the read (the K-index order is matched to the
@@ -100,6 +101,7 @@ __device__ __forceinline__ int64_t clip64(int64_t x, int64_t lo, int64_t hi) {
 }
 
 constexpr int kListCap = 2048;  // kept-block indices staged in LDS per window
+constexpr float kRescaleSlack = 8.0f;  // lazy online-softmax rescale threshold, log2 units
 
 // Copy the in-range entries of col_idx[*pos, end) into list in their original order, 256
 // entries per pass (wave w takes the w-th 64), stopping before a pass that could overflow
@@ -225,26 +227,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // The exponent reference m_run is raised only when this block's maximum exceeds it by more
+      // than kRescaleSlack (log2 units), so probabilities stay below 2^kRescaleSlack and the
+      // rescale of O and l is skipped for most blocks. Softmax is invariant to the reference,
+      // and l and O stay consistent with the same m_run, so only rounding differs.
+      if (__ballot(mx * scale_log2 > m_run + kRescaleSlack) != 0ull) {
+        const float m_new = fmaxf(m_run, mx * scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block
+        l_run *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nt][r] *= alpha;
+        m_run = m_new;
+      }
       float psum = 0.f;
       bf16x8 pf[8];
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -m_new));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -m_run));
           psum += p;
           pf[2 * jt + (r >> 3)][r & 7] = (__bf16)p;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.0f) != 0ull) {  // the running max moved for some query of the wave
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nt][r] *= alpha;
-      }
+      l_run += psum;
 
       // V(i) landed (the K prefetch just issued may still be in flight)
       wait_vmcnt<8>();
