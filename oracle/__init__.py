@@ -21,12 +21,12 @@ from .select import (BLOCK, MASS_BITS, block_scores, block_softmax, forced_block
                      mass_units, n_blocks, pool, select_mass, select_topk, sparse_select, to_csr,
                      topk_budget)
 from .attention import attention_dense, attention_masked, attention_rows
-from .energy import block_energy_rows, retained_mass
+from .energy import block_energy_rows, retained_mass, token_upper_bound
 from .vote import vote_masks
 
 __all__ = [
     "BLOCK", "MASS_BITS", "n_blocks", "pool", "block_scores", "block_softmax", "forced_blocks",
     "topk_budget", "select_topk", "mass_units", "mass_threshold_units", "select_mass", "to_csr",
     "sparse_select", "attention_rows", "attention_masked", "attention_dense", "block_energy_rows",
-    "retained_mass", "vote_masks",
+    "token_upper_bound", "retained_mass", "vote_masks",
 ]

@@ -42,6 +42,33 @@ def block_energy_rows(q, k, rows: Iterable[int], scale: Optional[float] = None,
     return out
 
 
+def token_upper_bound(q, k, rows: Iterable[int], budgets: Iterable[int],
+                      scale: Optional[float] = None, block: int = BLOCK) -> np.ndarray:
+    """Token-wise upper bound of the retained mass ([SparSTAR] "SparSTAR：为什么视频自回归的稀疏
+    注意力不能跨尺度复用？", Figure 3 compares per-scale block Top-K against it). Reading: for row r
+    with a budget of m_r key tokens (a mask of m_r / 128 blocks keeps m_r tokens per query), the
+    mean over the block's queries of the sum of that query's m_r largest probabilities under
+    the dense softmax. No mask keeping m_r tokens per query retains more, so a block mask's
+    retained mass is at most this value."""
+    bsz, heads, lq, d = q.shape
+    nqb = lq // block
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows, budgets = list(rows), list(budgets)
+    out = np.zeros(len(rows), dtype=np.float64)
+    for n, (r, m) in enumerate(zip(rows, budgets)):
+        bh, i = divmod(int(r), nqb)
+        b, h = divmod(bh, heads)
+        qi = np.asarray(q[b, h, i * block:(i + 1) * block], dtype=np.float64)
+        kk = np.asarray(k[b, h], dtype=np.float64)
+        logits = (qi @ kk.T) * scale
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        top = -np.sort(-p, axis=1)[:, :int(m)]
+        out[n] = top.sum(axis=1).mean()
+    return out
+
+
 def retained_mass(energy, kept) -> np.ndarray:
     """Sum of the block energies over the kept blocks of each row."""
     energy = np.asarray(energy, dtype=np.float64)

@@ -63,6 +63,24 @@ def _energy_no_divisor(q, k, rows, scale=None, block=oracle.BLOCK):
     return oen._orig_block_energy_rows(q, k, rows, scale, block) * block
 
 
+def _energy_transposed(q, k, rows, scale=None, block=oracle.BLOCK):
+    # sums over the key axis first and reports per-query-token mass (a transposed reduction)
+    e = oen._orig_block_energy_rows(q, k, rows, scale, block)
+    return e[:, ::-1].copy()
+
+
+def _upper_bound_smallest(q, k, rows, budgets, scale=None, block=oracle.BLOCK):
+    # the m smallest probabilities instead of the m largest
+    rows, budgets = list(rows), list(budgets)
+    n_keys = k.shape[-2]
+    return 1.0 - oen._orig_token_upper_bound(q, k, rows, [n_keys - m for m in budgets], scale,
+                                             block)
+
+
+def _upper_bound_off_by_one(q, k, rows, budgets, scale=None, block=oracle.BLOCK):
+    return oen._orig_token_upper_bound(q, k, rows, [max(m - 1, 0) for m in budgets], scale, block)
+
+
 def _softmax_weighted_unnormalised(logits, values):
     m = logits.max(axis=-1, keepdims=True)
     e = np.exp(logits - m)
@@ -83,6 +101,15 @@ MUTATIONS = {
                            [pins.test_energy_rows_sum_to_one]),
     "attention without normalisation": (oatt, "_softmax_weighted", _softmax_weighted_unnormalised,
                                         [pins.test_density_one_equals_dense_toy]),
+    "energy with reversed key blocks": (oen, "block_energy_rows", _energy_transposed,
+                                        [pins.test_energy_equals_sdpa_of_block_indicators,
+                                         pins.test_mean_field_identity]),
+    "upper bound from the smallest probabilities": (
+        oen, "token_upper_bound", _upper_bound_smallest,
+        [pins.test_token_upper_bound_brute_force_and_bounds]),
+    "upper bound one token short": (oen, "token_upper_bound", _upper_bound_off_by_one,
+                                    [pins.test_token_upper_bound_brute_force_and_bounds,
+                                     pins.test_token_upper_bound_mean_field_equals_block_topk]),
 }
 
 

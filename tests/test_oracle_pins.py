@@ -270,6 +270,70 @@ def test_mean_field_identity():
                                       oracle.select_mass(e_tok, forced, tau))
 
 
+def test_energy_equals_sdpa_of_block_indicators():
+    # With V the one-hot indicator of each key's block, attention output O[t, c] is the
+    # probability mass query t puts on block c; Eq. (5) is then the mean of O over the queries
+    # of the block. torch's float64 SDPA computes O independently of the oracle's code.
+    rng = np.random.default_rng(21)
+    bsz, heads, nqb, nkb, d = 1, 2, 2, 5, 16
+    q = rng.standard_normal((bsz, heads, nqb * BLOCK, d)) * 2.0
+    k = rng.standard_normal((bsz, heads, nkb * BLOCK, d)) * 2.0
+    ind = np.repeat(np.eye(nkb), BLOCK, axis=0)                      # [Lk, nKB]
+    v = np.broadcast_to(ind, (bsz, heads, nkb * BLOCK, nkb)).copy()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+    want = o.reshape(bsz * heads, nqb, BLOCK, nkb).mean(axis=2).reshape(-1, nkb)
+    got = oracle.block_energy_rows(q, k, rows=range(bsz * heads * nqb))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+def test_token_upper_bound_brute_force_and_bounds():
+    rng = np.random.default_rng(23)
+    # tiny blocks: brute force over every key subset of the budget's size
+    import itertools
+    blk, nqb, nkb, d = 2, 2, 4, 3
+    q = rng.standard_normal((1, 1, nqb * blk, d))
+    k = rng.standard_normal((1, 1, nkb * blk, d))
+    logits = (q[0, 0] @ k[0, 0].T) / math.sqrt(d)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    for m in range(1, nkb * blk + 1):
+        best = [max(p[t, list(c)].sum() for c in itertools.combinations(range(nkb * blk), m))
+                for t in range(nqb * blk)]
+        want = [np.mean(best[r * blk:(r + 1) * blk]) for r in range(nqb)]
+        got = oracle.token_upper_bound(q, k, rows=range(nqb), budgets=[m] * nqb, block=blk)
+        np.testing.assert_allclose(got, want, rtol=1e-12)
+    # full budget keeps everything; any block mask of the same size retains at most the bound
+    w = small_variants()["star_mid_small"]
+    qq, kk, _ = (t.double().numpy() for t in make_qkv(w.with_(heads=1), seed=6))
+    rows = range(w.n_q_blocks)
+    np.testing.assert_allclose(
+        oracle.token_upper_bound(qq, kk, rows, [w.lk] * w.n_q_blocks), 1.0, atol=1e-12)
+    e = oracle.block_energy_rows(qq, kk, rows)
+    for nkeep in (1, 3, 7):
+        kept = np.zeros_like(e, dtype=bool)
+        for r in range(e.shape[0]):
+            kept[r, rng.choice(e.shape[1], nkeep, replace=False)] = True
+        ub = oracle.token_upper_bound(qq, kk, rows, [nkeep * BLOCK] * e.shape[0])
+        assert (oracle.retained_mass(e, kept) <= ub + 1e-12).all()
+
+
+def test_token_upper_bound_mean_field_equals_block_topk():
+    # With every token equal to its block's vector, all queries of a block have the same
+    # probabilities, constant within a key block, so their best m = K * 128 tokens are the K
+    # blocks of largest energy and the bound equals the retained mass of the block Top-K mask.
+    rng = np.random.default_rng(29)
+    d, nqb, nkb, kk = 16, 2, 7, 3
+    q = np.repeat(rng.standard_normal((nqb, d)), BLOCK, axis=0)[None, None]
+    k = np.repeat(rng.standard_normal((nkb, d)) * 1.5, BLOCK, axis=0)[None, None]
+    e = oracle.block_energy_rows(q, k, rows=range(nqb))
+    kept = np.zeros_like(e, dtype=bool)
+    for r in range(nqb):
+        kept[r, np.argsort(-e[r], kind="stable")[:kk]] = True
+    ub = oracle.token_upper_bound(q, k, range(nqb), [kk * BLOCK] * nqb)
+    np.testing.assert_allclose(ub, oracle.retained_mass(e, kept), rtol=1e-12)
+
+
 # ---------------------------------------------------------------- attention
 
 def _torch_sdpa(q, k, v, kept):
