@@ -47,7 +47,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-attn fwd ms + MFMA util @72k-token scale; select ms + HBM GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_final_720p.json")
-ATTN_SOURCES = ("attn.hip", "common.hpp", "kernels.hpp")
+ATTN_SOURCES = ("attn.hip", "tile.hpp", "common.hpp", "kernels.hpp")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 

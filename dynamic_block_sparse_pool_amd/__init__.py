@@ -23,7 +23,8 @@ from . import _abi
 from ._abi import DBSP_BLOCK, DbspError
 
 __all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "topk_budget", "select_nnz_bound",
-           "select_workspace_bytes", "DbspError", "DBSP_BLOCK", "version"]
+           "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
+           "DbspError", "DBSP_BLOCK", "version"]
 
 
 @dataclasses.dataclass
@@ -209,3 +210,72 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
         _stream(q.device))
     _abi.check(st, "dbsp_sparse_attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def block_energy(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0,
+                 return_lse: bool = False, out: Optional[torch.Tensor] = None):
+    """Token-level block energy of every (query block, key block) pair of each head: the
+    attention probability mass between the two blocks under the dense softmax over all keys,
+    divided by 128. Returns a float32 [rows, n_k_blocks] tensor (and the per-query lse)."""
+    _check_device_tensor("q", q)
+    _check_device_tensor("k", k)
+    dims = _dims(q, k)
+    rows = dims.batch * dims.heads * (dims.lq // DBSP_BLOCK)
+    nkb = dims.lk // DBSP_BLOCK
+    if out is None:
+        out = torch.empty((rows, nkb), dtype=torch.float32, device=q.device)
+    elif out.shape != (rows, nkb) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [rows, n_k_blocks] tensor")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    st = _abi.load().dbsp_block_energy(_ptr(q), _ptr(k), ctypes.byref(dims), float(softmax_scale),
+                                       _ptr(out), _ptr(lse), _stream(q.device))
+    _abi.check(st, "dbsp_block_energy")
+    return (out, lse) if return_lse else out
+
+
+def _energy_dims(energy: torch.Tensor, batch: int, heads: int, n_k_blocks: int) -> _abi.Dims:
+    _check_device_tensor("energy", energy)
+    if energy.dtype != torch.float32 or energy.dim() != 2 or energy.shape[1] != n_k_blocks:
+        raise ValueError("energy must be float32 [rows, n_k_blocks]")
+    if energy.shape[0] % (batch * heads):
+        raise ValueError("energy rows are not a multiple of batch * heads")
+    nqb = energy.shape[0] // (batch * heads)
+    # head_dim and dtype do not enter these calls; the values only satisfy the shape check
+    return _abi.Dims(batch, heads, nqb * DBSP_BLOCK, n_k_blocks * DBSP_BLOCK, 128, _abi.DBSP_BF16)
+
+
+def retained_mass(energy: torch.Tensor, index: BlockIndex, batch: int = 1, heads: int = 1):
+    """Attention mass each row's mask keeps: the sum of its kept blocks' energies (float64)."""
+    dims = _energy_dims(energy, batch, heads, index.n_k_blocks)
+    if index.row_ptr.numel() != energy.shape[0] + 1:
+        raise ValueError("index and energy have different row counts")
+    mass = torch.empty(energy.shape[0], dtype=torch.float64, device=energy.device)
+    st = _abi.load().dbsp_retained_mass(_ptr(energy), ctypes.byref(dims), _ptr(index.row_ptr),
+                                        _ptr(index.col_idx), index.col_idx.numel(), _ptr(mass),
+                                        _stream(energy.device))
+    _abi.check(st, "dbsp_retained_mass")
+    return mass
+
+
+def select_energy(energy: torch.Tensor, mass: float, text_blocks=(0, 0),
+                  dense_extra_blocks=(0, 0), batch: int = 1, heads: int = 1) -> BlockIndex:
+    """Cumulative-mass selection on given block probabilities (e.g. token-level energies): per
+    row, the forced blocks and then the shortest (energy descending, index ascending) prefix whose
+    mass reaches `mass`, returned as an ascending CSR."""
+    nkb = energy.shape[1]
+    dims = _energy_dims(energy, batch, heads, nkb)
+    rows = energy.shape[0]
+    cap = select_nnz_bound(dims, _abi.DBSP_MASS, mass, text_blocks, dense_extra_blocks)
+    ws_n = ctypes.c_uint64()
+    lib = _abi.load()
+    _abi.check(lib.dbsp_select_energy_workspace_bytes(ctypes.byref(dims), ctypes.byref(ws_n)),
+               "dbsp_select_energy_workspace_bytes")
+    ws = torch.empty(max(ws_n.value, 1), dtype=torch.uint8, device=energy.device)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=energy.device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=energy.device)
+    st = lib.dbsp_select_energy(_ptr(energy), ctypes.byref(dims), _range(text_blocks),
+                                _range(dense_extra_blocks), float(mass), _ptr(row_ptr),
+                                _ptr(col_idx), col_idx.numel(), _ptr(ws), ws.numel(),
+                                _stream(energy.device))
+    _abi.check(st, "dbsp_select_energy")
+    return BlockIndex(row_ptr, col_idx, dims.lq // DBSP_BLOCK, nkb, None)

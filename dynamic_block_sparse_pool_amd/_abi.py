@@ -49,6 +49,11 @@ SIGNATURES = {
                                   _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _PDims, _vp, _vp, _i64, _f32, _vp, _i32, _vp,
                                     _vp]),
+    "dbsp_block_energy": (_i32, [_vp, _vp, _PDims, _f32, _vp, _vp, _vp]),
+    "dbsp_retained_mass": (_i32, [_vp, _PDims, _vp, _vp, _i64, _vp, _vp]),
+    "dbsp_select_energy": (_i32, [_vp, _PDims, Range, Range, _f64, _vp, _vp, _i64, _vp, _u64,
+                                  _vp]),
+    "dbsp_select_energy_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
 }
 
 _lib = None

@@ -10,7 +10,9 @@
 
 namespace {
 
-constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kVersion = 110;  // 0.1.1: token-level energy, retained mass, energy selection
+// bf16 attention addresses a head's K and V with 32-bit byte offsets (block index x 32 KiB)
+constexpr int32_t kMaxBf16KeyBlocks = 65535;
 
 bool shape_ok(const dbsp_dims* d) {
   if (!d) return false;
@@ -117,6 +119,16 @@ WorkspaceLayout layout_of(const dbsp_dims* d, int32_t mode) {
     off = align256(off + bh * nqb * ((nkb + 63) / 64) * sizeof(uint64_t));
   }
   w.total = off;
+  return w;
+}
+
+// dbsp_select_energy: per-row counts and kept bitmasks only.
+WorkspaceLayout energy_select_layout(const dbsp_dims* d) {
+  WorkspaceLayout w{};
+  const uint64_t rows = (uint64_t)rows_of(d), nkb = d->lk / DBSP_BLOCK;
+  w.counts = 0;
+  w.masks = align256(rows * sizeof(int32_t));
+  w.total = align256(w.masks + rows * ((nkb + 63) / 64) * sizeof(uint64_t));
   return w;
 }
 
@@ -236,6 +248,8 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
     return DBSP_ERR_INVALID_ARG;
   if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
   if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
+  if (dims->dtype == DBSP_BF16 && dims->lk / DBSP_BLOCK > kMaxBf16KeyBlocks)
+    return DBSP_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.f ? softmax_scale
                                           : (float)(1.0 / sqrt((double)dims->head_dim));
   dbsp::AttnArgs a{};
@@ -255,6 +269,87 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
   a.lse = lse_out;
   if (dbsp::launch_attn(a, dims->head_dim, dims->dtype == DBSP_BF16,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, float softmax_scale,
+                          float* energy, float* lse_out, void* stream) {
+  if (!shape_ok(dims) || !q || !k || !energy) return DBSP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || ((uintptr_t)energy & 3u) || ((uintptr_t)lse_out & 3u))
+    return DBSP_ERR_INVALID_ARG;
+  if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
+  if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
+  if (dims->lk / DBSP_BLOCK > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  const float scale = softmax_scale > 0.f ? softmax_scale
+                                          : (float)(1.0 / sqrt((double)dims->head_dim));
+  dbsp::EnergyArgs a{};
+  a.q = q;
+  a.k = k;
+  a.nqb = dims->lq / DBSP_BLOCK;
+  a.nkb = dims->lk / DBSP_BLOCK;
+  a.rows = rows_of(dims);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.energy = energy;
+  a.lse = lse_out;
+  if (dbsp::launch_energy(a, dims->head_dim, dims->dtype == DBSP_BF16,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_retained_mass(const float* energy, const dbsp_dims* dims, const int32_t* row_ptr,
+                           const int32_t* col_idx, int64_t col_capacity, double* mass,
+                           void* stream) {
+  if (!shape_ok(dims) || !energy || !row_ptr || !mass) return DBSP_ERR_INVALID_ARG;
+  if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
+  if (dbsp::launch_retained_mass(energy, row_ptr, col_idx, col_capacity, dims->lk / DBSP_BLOCK,
+                                 rows_of(dims), mass, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_select_energy_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes) {
+  if (!shape_ok(dims) || !bytes) return DBSP_ERR_INVALID_ARG;
+  *bytes = energy_select_layout(dims).total;
+  return DBSP_OK;
+}
+
+int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_range text_blocks,
+                           dbsp_range dense_extra_blocks, double mass, int32_t* row_ptr,
+                           int32_t* col_idx, int64_t col_capacity, void* workspace,
+                           uint64_t workspace_bytes, void* stream) {
+  if (!shape_ok(dims) || !energy || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
+  const int32_t nkb = dims->lk / DBSP_BLOCK;
+  if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  int64_t bound;
+  const int32_t st = nnz_bound(dims, DBSP_MASS, mass, text_blocks, dense_extra_blocks, -1, &bound);
+  if (st != DBSP_OK) return st;
+  if (bound > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  if (col_capacity < bound) return DBSP_ERR_CAPACITY;
+  const WorkspaceLayout wl = energy_select_layout(dims);
+  if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255u))
+    return DBSP_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  dbsp::SelectArgs a{};
+  a.nqb = dims->lq / DBSP_BLOCK;
+  a.nkb = nkb;
+  a.t0 = text_blocks.begin;
+  a.t1 = text_blocks.end;
+  a.e0 = dense_extra_blocks.begin;
+  a.e1 = dense_extra_blocks.end;
+  a.mode = DBSP_MASS;
+  a.keep_all = mass >= 1.0;
+  a.theta = (uint64_t)ceil(mass * 4611686018427387904.0);  // tau * 2^62
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_capacity = col_capacity;
+  a.counts = reinterpret_cast<int32_t*>(ws + wl.counts);
+  a.masks = reinterpret_cast<uint64_t*>(ws + wl.masks);
+  a.words = (nkb + 63) / 64;
+  a.n_rows = rows_of(dims);
+  if (dbsp::launch_select_energy(a, energy, static_cast<hipStream_t>(stream)) != hipSuccess)
     return DBSP_ERR_HIP;
   return DBSP_OK;
 }

@@ -1,0 +1,259 @@
+// Token-level block energy and the retained attention mass of a block mask.
+//
+// Sources: [CalibAtt] "Accelerating Text-to-Video Generation with Calibrated Sparse Attention",
+// key design 1, Eq. (5): the energy of query block r and key block c is the attention
+// probability mass between them, summed over the block's queries and keys and divided by the
+// block size; every query-block row of E sums to 1. The page computes it with a custom kernel
+// that never materialises the attention matrix. [SparSTAR] "SparSTAR：为什么视频自回归的稀疏注意力
+// 不能跨尺度复用？", Figures 3 and 4, report the retained mass of masks (the sum of E over the kept
+// blocks).
+//
+// block_energy_bf16_kernel (bf16, head_dim 128): one workgroup of 4 waves per (batch, head,
+// query block) row, wave w owning queries [32 w, 32 w + 32) with the same S^T = K Q^T tiling on
+// 32x32x16 bf16 MFMAs as the attention kernel. Two sweeps over every key block of the head:
+//   1. running maximum and sum of exp2(s - m) per query, giving its log-sum-exp (log2 units);
+//   2. per key block, the sum of exp2(s - lse) over the block's 128 x 128 pairs: each lane adds
+//      its 64 values, the wave adds its lanes in a fixed DPP order, and the four wave totals are
+//      added in wave order and divided by 128 (deterministic, no atomics).
+// K tiles are double-buffered in LDS: the DMA of the next block runs while this one is scored.
+// Every row of a head walks the same blocks in the same order, so the K stream is shared
+// through L2 by the workgroups of a head that run together.
+//
+// block_energy_f32_kernel (fp32, head_dim 64 or 128): one thread per query, K block in LDS,
+// the same two sweeps with plain FMA arithmetic and a tree reduction per key block.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tile.hpp"
+
+namespace dbsp {
+
+// S^T tiles of one key block: sacc[jt] holds keys 32 jt .. 32 jt + 31 (rows) x the wave's 32
+// queries; qf is the B operand (queries as columns) held in registers.
+__device__ __forceinline__ void qk_block(const uint16_t* k_tile, const bf16x8 (&qf)[8], int l32,
+                                         int h, f32x16 (&sacc)[4]) {
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
+    const int kr = 32 * jt + l32;
+    const uint16_t* krow = k_tile + kr * 128;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + k_swz(kr, 2 * s + h) * 8);
+      sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[jt], 0, 0, 0);
+    }
+  }
+}
+
+// Step g of the 2 * nkb steps (block g mod nkb) lives in LDS buffer g & 1. Waits for it, lets
+// every wave finish the previous step, and starts the DMA of step g + 1 into the other buffer
+// (the final step re-fetches its own block: an unconditional issue keeps the compiler's DMA wait
+// tracking exact).
+__device__ __forceinline__ const uint16_t* energy_step_begin(int g, int nkb, uint16_t* k_lds,
+                                                             __amdgpu_buffer_rsrc_t kbuf, int w,
+                                                             const DmaOffsets& dmo) {
+  constexpr int kTileBytes = kBlock * 128 * 2;
+  wait_vmcnt<0>();
+  wait_lgkmcnt0();
+  wg_barrier();
+  const int gn = g + 1 < 2 * nkb ? g + 1 : g;
+  const int cn = gn < nkb ? gn : gn - nkb;
+  tile_dma<false>(kbuf, cn * kTileBytes, k_lds + ((g + 1) & 1) * (kBlock * 128), w, dmo);
+  return k_lds + (g & 1) * (kBlock * 128);
+}
+
+__global__ __launch_bounds__(256, 2) void block_energy_bf16_kernel(
+    const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, int nqb, int nkb,
+    float scale_log2, float* __restrict__ energy, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * kBlock * 128];
+  __shared__ float part[4][64];
+
+  const int64_t row = blockIdx.x;
+  const int64_t bh = row / nqb;
+  const int qb = (int)(row - bh * nqb);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int64_t lq = (int64_t)nqb * kBlock;
+  const int64_t lk = (int64_t)nkb * kBlock;
+  const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kg + bh * lk * 128, (uint32_t)(lk * 256));
+  const DmaOffsets dmo = dma_offsets(lane);
+
+  // Q^T as the B operand: lane (h, l32) holds query 32 w + l32, dims 16 s + 8 h .. +7
+  const int64_t qtok = bh * lq + (int64_t)qb * kBlock + 32 * w + l32;
+  bf16x8 qf[8];
+  {
+    const uint16_t* qr = qg + qtok * 128 + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
+  }
+
+  tile_dma<false>(kbuf, 0, k_lds, w, dmo);
+
+  // sweep 1: log-sum-exp per query (lanes l32 and l32 + 32 hold halves of the same query)
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int g = 0; g < nkb; ++g) {
+    const uint16_t* kt = energy_step_begin(g, nkb, k_lds, kbuf, w, dmo);
+    f32x16 sacc[4];
+    qk_block(kt, qf, l32, h, sacc);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    float ps = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ps += __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -m_new));
+    l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + ps;
+    m_run = m_new;
+  }
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float lse2 = m_run + __log2f(l_tot);
+  if (lse && h == 0) lse[qtok] = lse2 * 0.69314718055994531f;
+
+  // sweep 2: block energies; lane c mod 64 of `acc` collects the wave's total of block c
+  float acc = 0.f;
+  for (int g = nkb; g < 2 * nkb; ++g) {
+    const int c = g - nkb;
+    const uint16_t* kt = energy_step_begin(g, nkb, k_lds, kbuf, w, dmo);
+    f32x16 sacc[4];
+    qk_block(kt, qf, l32, h, sacc);
+    float ps = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ps += __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -lse2));
+    const float t = wave_total_f32(ps);
+    acc = lane == (c & 63) ? t : acc;
+    if ((c & 63) == 63 || c == nkb - 1) {  // uniform: flush 64 blocks (or the tail)
+      part[w][lane] = acc;
+      wait_lgkmcnt0();
+      wg_barrier();
+      const int cc = (c & ~63) + lane;
+      if (w == 0 && cc <= c)
+        energy[row * nkb + cc] =
+            (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) * (1.0f / kBlock);
+    }
+  }
+  wait_vmcnt<0>();
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void block_energy_f32_kernel(EnergyArgs a) {
+  __shared__ float k_lds[kBlock][D];
+  __shared__ float red[kBlock];
+  const int64_t row = blockIdx.x;
+  const int64_t bh = row / a.nqb;
+  const int qb = (int)(row - bh * a.nqb);
+  const int t = threadIdx.x;
+  const int64_t lq = (int64_t)a.nqb * kBlock;
+  const int64_t lk = (int64_t)a.nkb * kBlock;
+  const int64_t qtok = bh * lq + (int64_t)qb * kBlock + t;
+  const float* qp = static_cast<const float*>(a.q) + qtok * D;
+  const float* kp = static_cast<const float*>(a.k) + bh * lk * D;
+  float qv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) qv[d] = qp[d];
+
+  float m_run = -INFINITY, l_run = 0.f, lse2 = 0.f;
+  for (int g = 0; g < 2 * a.nkb; ++g) {
+    const int c = g < a.nkb ? g : g - a.nkb;
+    const float* kb = kp + (int64_t)c * kBlock * D;
+    for (int i = t; i < kBlock * D; i += kBlock) (&k_lds[0][0])[i] = kb[i];
+    __syncthreads();
+    if (g < a.nkb) {
+      for (int j0 = 0; j0 < kBlock; j0 += 32) {  // chunks of 32 keys keep the scores in registers
+        float s[32];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          float dot = 0.f;
+#pragma unroll
+          for (int d = 0; d < D; ++d) dot = fmaf(qv[d], k_lds[j0 + j][d], dot);
+          s[j] = dot * a.scale_log2;
+          mx = fmaxf(mx, s[j]);
+        }
+        const float m_new = fmaxf(m_run, mx);
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) ps += __builtin_amdgcn_exp2f(s[j] - m_new);
+        l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + ps;
+        m_run = m_new;
+      }
+      if (g == a.nkb - 1) {
+        lse2 = m_run + __log2f(l_run);
+        if (a.lse) a.lse[qtok] = lse2 * 0.69314718055994531f;
+      }
+    } else {
+      float ps = 0.f;
+      for (int j = 0; j < kBlock; ++j) {
+        float dot = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) dot = fmaf(qv[d], k_lds[j][d], dot);
+        ps += __builtin_amdgcn_exp2f(fmaf(dot, a.scale_log2, -lse2));
+      }
+      red[t] = ps;
+      __syncthreads();
+      for (int off = kBlock / 2; off > 0; off >>= 1) {
+        if (t < off) red[t] += red[t + off];
+        __syncthreads();
+      }
+      if (t == 0) a.energy[row * a.nkb + c] = red[0] * (1.0f / kBlock);
+    }
+    __syncthreads();
+  }
+}
+
+// Retained mass of a CSR mask: one wave per row adds the energies of the row's in-range entries
+// in float64 (lane-strided partial sums, then a fixed butterfly order).
+__global__ __launch_bounds__(256) void retained_mass_kernel(
+    const float* __restrict__ energy, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, int64_t col_capacity, int nkb, int64_t rows,
+    double* __restrict__ mass) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t beg = clip64(row_ptr[row], 0, col_capacity);
+  const int64_t end = clip64(row_ptr[row + 1], beg, col_capacity);
+  double s = 0.0;
+  for (int64_t e = beg + lane; e < end; e += 64) {
+    const int c = col_idx[e];
+    if (c >= 0 && c < nkb) s += (double)energy[row * nkb + c];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) mass[row] = s;
+}
+
+hipError_t launch_energy(const EnergyArgs& a, int head_dim, bool bf16, hipStream_t stream) {
+  const dim3 grid((unsigned)a.rows);
+  if (bf16 && head_dim == 128)
+    block_energy_bf16_kernel<<<grid, 256, 0, stream>>>(
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.nqb, a.nkb,
+        a.scale_log2, a.energy, a.lse);
+  else if (!bf16 && head_dim == 64)
+    block_energy_f32_kernel<64><<<grid, kBlock, 0, stream>>>(a);
+  else if (!bf16 && head_dim == 128)
+    block_energy_f32_kernel<128><<<grid, kBlock, 0, stream>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_retained_mass(const float* energy, const int32_t* row_ptr,
+                                const int32_t* col_idx, int64_t col_capacity, int nkb,
+                                int64_t rows, double* mass, hipStream_t stream) {
+  retained_mass_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(
+      energy, row_ptr, col_idx, col_capacity, nkb, rows, mass);
+  return hipGetLastError();
+}
+
+}  // namespace dbsp

@@ -44,11 +44,26 @@ struct AttnArgs {
   float* lse;
 };
 
+struct EnergyArgs {
+  const void* q;
+  const void* k;
+  int nqb, nkb;
+  int64_t rows;
+  float scale_log2;  // softmax_scale * log2(e)
+  float* energy;     // [rows, nkb]
+  float* lse;        // nullable [rows * 128]
+};
+
 hipError_t launch_pool(const void* q, const void* k, uint16_t* qsplit, uint16_t* ksplit,
                        int64_t nq_blocks, int64_t nk_blocks, int nkb, int head_dim, bool bf16,
                        hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, bool bf16,
                          hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_energy(const EnergyArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_retained_mass(const float* energy, const int32_t* row_ptr,
+                                const int32_t* col_idx, int64_t col_capacity, int nkb,
+                                int64_t rows, double* mass, hipStream_t stream);
+hipError_t launch_select_energy(const SelectArgs& a, const float* energy, hipStream_t stream);
 
 }  // namespace dbsp

@@ -323,28 +323,12 @@ __device__ __forceinline__ void select_topk_row(const SelectArgs& a, const float
   }
 }
 
-// Cumulative-mass selection of one row; writes the kept bitmask words and count.
+// Cumulative-mass selection of one row from its block probabilities p (slot e of lane l is key
+// block 64 e + l; entries past nkb are ignored); writes the kept bitmask words and count.
 template <int S>
-__device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float* srow,
-                                                int64_t row, int lane) {
+__device__ __forceinline__ void select_mass_probs(const SelectArgs& a, const float (&prob)[S],
+                                                  int64_t row, int lane) {
   const int nkb = a.nkb;
-  float val[S];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < S; ++e) {
-    const int c = e * 64 + lane;
-    val[e] = c < nkb ? srow[c] : -INFINITY;
-    mx = fmaxf(mx, val[e]);
-  }
-  mx = wave_max_dpp(mx);
-  float part = 0.f;
-#pragma unroll
-  for (int e = 0; e < S; ++e) {
-    const int c = e * 64 + lane;
-    val[e] = c < nkb ? __expf(val[e] - mx) : 0.f;
-    part += val[e];
-  }
-  const float inv = 1.0f / wave_total_f32(part);
   uint64_t u[S];
   uint32_t key[S];
   uint64_t fsum = 0, csum = 0;
@@ -353,8 +337,7 @@ __device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float
   for (int e = 0; e < S; ++e) {
     const int c = e * 64 + lane;
     const bool valid = c < nkb;
-    const float p = val[e] * inv;
-    if (valid && a.scores_out) a.scores_out[row * nkb + c] = p;
+    const float p = prob[e];
     const bool f = valid && is_forced(c, a);
     u[e] = valid ? mass_units(p) : 0ull;
     key[e] = (valid && !f) ? order_key(p) : 0u;
@@ -425,6 +408,38 @@ __device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float
     cnt += (uint32_t)__popcll(km);
   }
   if (lane == 0) a.counts[row] = (int32_t)cnt;
+}
+
+// Pooled-score mass mode: p = softmax over the row's scores (written to scores_out when given),
+// then the cumulative-mass selection.
+template <int S>
+__device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float* srow,
+                                                int64_t row, int lane) {
+  const int nkb = a.nkb;
+  float val[S];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    val[e] = c < nkb ? srow[c] : -INFINITY;
+    mx = fmaxf(mx, val[e]);
+  }
+  mx = wave_max_dpp(mx);
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    val[e] = c < nkb ? __expf(val[e] - mx) : 0.f;
+    part += val[e];
+  }
+  const float inv = 1.0f / wave_total_f32(part);
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    val[e] *= inv;
+    if (c < nkb && a.scores_out) a.scores_out[row * nkb + c] = val[e];
+  }
+  select_mass_probs<S>(a, val, row, lane);
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin by id, so id b runs on XCD b % 8. Work item
@@ -516,6 +531,52 @@ __global__ __launch_bounds__(256) void fill_csr_kernel(const uint64_t* __restric
   }
 }
 
+// Token-level mass mode: the block probabilities of each row are given (block energies, one
+// row per wave, four rows per workgroup).
+template <int S>
+__global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const float* energy) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.n_rows) return;
+  const int lane = threadIdx.x & 63;
+  float p[S];
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const int c = e * 64 + lane;
+    p[e] = c < a.nkb ? energy[row * a.nkb + c] : 0.f;
+  }
+  select_mass_probs<S>(a, p, row, lane);
+}
+
+static hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream) {
+  scan_counts_kernel<<<1, 1024, 0, stream>>>(a.counts, a.row_ptr, a.n_rows);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  fill_csr_kernel<<<(unsigned)((a.n_rows + 3) / 4), 256, 0, stream>>>(
+      a.masks, a.row_ptr, a.col_idx, a.n_rows, a.words, a.col_capacity);
+  return hipGetLastError();
+}
+
+static hipError_t launch_select_energy_rows(const SelectArgs& a, const float* energy,
+                                            hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n_rows + 3) / 4));
+  const int slots = (a.nkb + 63) / 64;
+#define DBSP_SLOTS(N)                                              \
+  if (slots <= N) {                                                \
+    select_energy_kernel<N><<<grid, 256, 0, stream>>>(a, energy);  \
+    return hipGetLastError();                                      \
+  }
+  DBSP_SLOTS(1) DBSP_SLOTS(2) DBSP_SLOTS(4) DBSP_SLOTS(6) DBSP_SLOTS(8) DBSP_SLOTS(10)
+  DBSP_SLOTS(12) DBSP_SLOTS(16) DBSP_SLOTS(20) DBSP_SLOTS(24) DBSP_SLOTS(28) DBSP_SLOTS(32)
+#undef DBSP_SLOTS
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select_energy(const SelectArgs& a, const float* energy, hipStream_t stream) {
+  const hipError_t err = launch_select_energy_rows(a, energy, stream);
+  if (err != hipSuccess) return err;
+  return launch_counts_to_csr(a, stream);
+}
+
 template <typename T, int D, int MODE>
 static hipError_t launch_score_select_dm(const SelectArgs& a, int64_t bh, hipStream_t stream) {
   const int64_t items = bh * ((a.nqb + kRowsPerWG - 1) / kRowsPerWG);
@@ -552,12 +613,7 @@ hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, bool bf1
   else
     return hipErrorInvalidValue;
   if (err != hipSuccess || a.mode == 0) return err;
-  const int64_t rows = bh * a.nqb;
-  scan_counts_kernel<<<1, 1024, 0, stream>>>(a.counts, a.row_ptr, rows);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  fill_csr_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a.masks, a.row_ptr, a.col_idx,
-                                                                  rows, a.words, a.col_capacity);
-  return hipGetLastError();
+  return launch_counts_to_csr(a, stream);
 }
 
 }  // namespace dbsp

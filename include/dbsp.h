@@ -8,6 +8,12 @@
  *   dbsp_sparse_attn_fwd  Q, K, V, CSR -> O (and optionally the log-sum-exp), attending only
  *                         to the tokens of the kept key blocks.
  *
+ * Beside it, the token-level quantities the pages measure masks with:
+ *
+ *   dbsp_block_energy     Q, K -> the token-level energy of every (query block, key block) pair.
+ *   dbsp_retained_mass    energy, CSR -> the attention mass each row's mask keeps.
+ *   dbsp_select_energy    energy -> a CSR by the cumulative-mass rule on token-level energies.
+ *
  * What the calls compute follows two pages:
  *   [SparSTAR] "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis", in the
  *       pchao.org digest titled "SparSTAR：为什么视频自回归的稀疏注意力不能跨尺度复用？", section
@@ -157,11 +163,68 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
  * skipped and row extents are clipped to [0, col_capacity).
  * o is [batch, heads, lq, head_dim] in o_dtype (DBSP_F32 or DBSP_BF16, round to nearest even).
  * lse_out, if not NULL, is float32 [batch, heads, lq].
+ * Limits: bf16 inputs need lk / 128 <= 65535 (a head's K and V are addressed with 32-bit byte
+ * offsets); DBSP_ERR_UNSUPPORTED otherwise.
  */
 int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
                              const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
                              float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
                              void* stream);
+
+/*
+ * Token-level block energy ([CalibAtt] key design 1, Eq. (5)).
+ *
+ * For each row r = (b, h, i) and each key block c of the same (b, h):
+ *   energy[r][c] = (1 / 128) * sum over queries t of block i and keys j of block c of P_tj,
+ *   P_tj = softmax over ALL lk keys of (q_t . k_j * softmax_scale)
+ * so each row sums to 1 (up to rounding). softmax_scale <= 0 means 1 / sqrt(head_dim). The
+ * attention matrix is never stored: the kernel makes two passes over the keys (log-sum-exp per
+ * query, then the block sums). Arithmetic as dbsp_sparse_attn_fwd (bf16 matrix-core products
+ * with float32 accumulation; float32 for float32 inputs); the block sums add in a fixed order,
+ * so results are bit-reproducible.
+ *
+ * q, k: as for dbsp_sparse_attn_fwd (no V). energy: device float32 [rows, lk / 128].
+ * lse_out, if not NULL: device float32 [batch, heads, lq], the natural-log log-sum-exp of each
+ * query over all keys. Cost: 4 * 128 * 128 * head_dim FLOP per (row, key block) pair, i.e. the
+ * dense QK^T product twice.
+ * Errors: DBSP_ERR_INVALID_ARG for null or misaligned pointers, a bad shape or a non-finite
+ * scale; DBSP_ERR_UNSUPPORTED for other dtype / head_dim pairs or lk / 128 > DBSP_MAX_KEY_BLOCKS.
+ */
+int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, float softmax_scale,
+                          float* energy, float* lse_out, void* stream);
+
+/*
+ * Retained attention mass of a block mask ([SparSTAR] Figures 3 and 4 report it per scale and
+ * clip): mass[r] = sum over the in-range entries c of CSR row r of energy[r][c], added in float64.
+ * energy: device float32 [rows, lk / 128] (from dbsp_block_energy); row_ptr / col_idx /
+ * col_capacity as for dbsp_sparse_attn_fwd (entries outside [0, lk / 128) skipped, extents
+ * clipped); mass: device float64 [rows]. Duplicate entries count twice.
+ * Errors: DBSP_ERR_INVALID_ARG for null pointers, a bad shape or a negative capacity.
+ */
+int32_t dbsp_retained_mass(const float* energy, const dbsp_dims* dims, const int32_t* row_ptr,
+                           const int32_t* col_idx, int64_t col_capacity, double* mass,
+                           void* stream);
+
+/*
+ * Token-level mass-mode selection: the cumulative-mass rule of dbsp_sparse_select's DBSP_MASS
+ * mode ([CalibAtt] key design 1: keep the shortest prefix of the energy-sorted row that reaches
+ * the threshold, back in index order) applied to given block probabilities, such as the token-level
+ * energies of dbsp_block_energy, instead of the pooled-score softmax. Step 4b of
+ * dbsp_sparse_select with p_ic = energy[r][c] (fixed-point masses floor(p * 2^62), forced
+ * blocks first, ties to the lower index, keep all if the row never reaches tau, tau = 1 keeps
+ * all); step 5 for the output. energy: device float32 [rows, lk / 128], values in [0, 1].
+ * workspace: at least dbsp_select_energy_workspace_bytes bytes of device memory, 256-byte
+ * aligned. The nnz bound is rows * (lk / 128) (dbsp_select_nnz_bound in DBSP_MASS mode).
+ * Errors: as dbsp_sparse_select (ranges, tau in (0, 1], capacity, workspace); DBSP_ERR_UNSUPPORTED
+ * for lk / 128 > DBSP_MAX_KEY_BLOCKS or an nnz bound above INT32_MAX.
+ */
+int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_range text_blocks,
+                           dbsp_range dense_extra_blocks, double mass, int32_t* row_ptr,
+                           int32_t* col_idx, int64_t col_capacity, void* workspace,
+                           uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes dbsp_select_energy needs for dims (per-row counts and kept bitmasks). */
+int32_t dbsp_select_energy_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,11 @@ BF16_O_MAX = 2e-2          # bf16 inputs: max |O - O_ref| ...
 BF16_O_MEAN = 2e-3         # ... and mean |O - O_ref|
 F32_LSE = 1e-5
 BF16_LSE = 1e-3
+# token-level block energy (dense softmax, fp32 accumulation on both input types)
+TOK_E_RTOL = 2e-4          # |E - E_ref| <= TOK_E_RTOL * E_ref + TOK_E_ATOL
+TOK_E_ATOL = 1e-7
+TOK_ROW_SUM = 1e-4         # |sum_c E_rc - 1|
+TOK_LSE = 1e-4             # per-query log-sum-exp over all keys (natural log)
 
 
 def host(t: torch.Tensor) -> np.ndarray:
@@ -106,3 +111,12 @@ def topk_near_tie_ok(kept_gpu, kept_ref, s_ref, forced, tol):
         assert (np.abs(s_ref[r][only_gpu] - lo) <= 2 * tol[r][only_gpu]).all()
         assert (np.abs(s_ref[r][only_ref] - lo) <= 2 * tol[r][only_ref]).all()
     return diff_rows.size
+
+
+def check_token_energy(e_gpu: np.ndarray, e_ref: np.ndarray):
+    """Token-level energies against the oracle's Eq. (5) on the same rows."""
+    err = np.abs(e_gpu - e_ref)
+    tol = TOK_E_RTOL * e_ref + TOK_E_ATOL
+    assert (err <= tol).all(), f"energy mismatch: worst excess {float((err - tol).max()):.3e}"
+    assert np.abs(e_gpu.sum(axis=-1) - 1.0).max() <= TOK_ROW_SUM
+    assert (e_gpu >= 0).all()

@@ -170,3 +170,49 @@ def test_attn_rejects_bad_arguments(lib):
         assert attn(**kw) == E.DBSP_ERR_INVALID_ARG, kw
     assert attn(dims=_abi.Dims(1, 2, 256, 1024, 64, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
     assert attn(dims=_abi.Dims(1, 2, 256, 1024, 32, E.DBSP_F32)) == E.DBSP_ERR_UNSUPPORTED
+
+
+def test_energy_calls_reject_bad_arguments(lib):
+    E = _abi
+    good = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_BF16)
+
+    def energy(dims=good, q=FAKE, k=FAKE, out=FAKE, lse=None, scale=0.0):
+        return lib.dbsp_block_energy(q, k, ctypes.byref(dims), scale, out, lse, None)
+
+    for kw in ({"q": None}, {"k": None}, {"out": None}, {"scale": float("nan")},
+               {"q": ctypes.c_void_p((1 << 20) + 8)}, {"out": ctypes.c_void_p((1 << 20) + 2)},
+               {"dims": _abi.Dims(1, 2, 200, 1024, 128, E.DBSP_BF16)}):
+        assert energy(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    assert energy(dims=_abi.Dims(1, 2, 256, 1024, 64, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+    assert energy(dims=_abi.Dims(1, 1, 256, 2049 * 128, 128, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+
+    def mass(dims=good, e=FAKE, rp=FAKE, ci=FAKE, cap=16, out=FAKE):
+        return lib.dbsp_retained_mass(e, ctypes.byref(dims), rp, ci, cap, out, None)
+
+    for kw in ({"e": None}, {"rp": None}, {"out": None}, {"cap": -1}, {"ci": None}):
+        assert mass(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+
+    def sel(dims=good, e=FAKE, tau=0.9, text=(0, 1), extra=(0, 0), rp=FAKE, ci=FAKE,
+            cap=1 << 40, ws=FAKE, ws_bytes=1 << 40):
+        return lib.dbsp_select_energy(e, ctypes.byref(dims), _abi.Range(*text), _abi.Range(*extra),
+                                      tau, rp, ci, cap, ws, ws_bytes, None)
+
+    for kw in ({"e": None}, {"rp": None}, {"ci": None}, {"tau": 0.0}, {"tau": 1.5},
+               {"text": (0, 9)}, {"text": (0, 3), "extra": (2, 5)}):
+        assert sel(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    # 2 heads x 2 query blocks x 8 key blocks
+    assert sel(cap=31) == E.DBSP_ERR_CAPACITY
+    assert sel(ws=None) == E.DBSP_ERR_WORKSPACE
+    assert sel(ws_bytes=16) == E.DBSP_ERR_WORKSPACE
+    assert sel(dims=_abi.Dims(1, 1, 256, 2049 * 128, 128, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+    ws = ctypes.c_uint64()
+    assert lib.dbsp_select_energy_workspace_bytes(ctypes.byref(good), ctypes.byref(ws)) == 0
+    rows, words = 4, 1
+    assert ws.value >= rows * 4 + rows * words * 8
+
+
+def test_attn_rejects_too_many_bf16_key_blocks(lib):
+    E = _abi
+    dims = _abi.Dims(1, 1, 128, 65536 * 128, 128, E.DBSP_BF16)
+    assert lib.dbsp_sparse_attn_fwd(FAKE, FAKE, FAKE, ctypes.byref(dims), FAKE, FAKE, 16, 0.0, FAKE,
+                                    E.DBSP_F32, None, None) == E.DBSP_ERR_UNSUPPORTED
