@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
+    ap.add_argument("--suite", choices=("hot", "energy"), default="hot",
+                    help="hot: the selection + attention step (default); energy: the token-level "
+                         "block energy, energy-driven selection and retained mass (one JSON line)")
     ap.add_argument("--only-copy", action="store_true",
                     help="run only the 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--cold-iters", type=int, default=8,
@@ -169,6 +172,101 @@ def cpu_baseline(w, q, k, v, row_ptr, col_idx, nnz, flop_per_pair, budget_s):
     }
 
 
+def energy_suite(args, torch):
+    """Token-level block energy (two dense sweeps of Q K^T per row), the cumulative-mass
+    selection on those energies, and the retained mass of that mask and of the pooled
+    selection's mask. Default workload: the DiT mass-mode configuration, where the token-level
+    energy is the pages' own calibration quantity."""
+    import numpy as np
+    import dynamic_block_sparse_pool_amd as dbsp
+    from synth import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload or "dit_mass"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, _ = make_qkv(w, device=dev, seed=args.seed)
+    rows, nkb = w.rows, w.n_k_blocks
+    energy = torch.empty((rows, nkb), dtype=torch.float32, device=dev)
+    tau = w.param if w.mode == "mass" else 0.9
+    kw = dict(density=w.param) if w.mode == "topk" else dict(mass=w.param)
+    pooled = dbsp.sparse_select(q, k, w.text, w.extra, **kw)
+    for _ in range(max(args.warmup, 1)):
+        dbsp.block_energy(q, k, out=energy)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        dbsp.block_energy(q, k, out=energy)
+        e[1].record()
+        idx = dbsp.select_energy(energy, tau, w.text, w.extra, batch=w.batch, heads=w.heads)
+        e[2].record()
+        mass_tok = dbsp.retained_mass(energy, idx, batch=w.batch, heads=w.heads)
+        e[3].record()
+    torch.cuda.synchronize()
+    e_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    s_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    m_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    mass_pooled = dbsp.retained_mass(energy, pooled, batch=w.batch, heads=w.heads)
+    nnz_tok, nnz_pool = idx.nnz(), pooled.nnz()
+    flop = rows * nkb * 4 * 128 * 128 * w.head_dim
+    e_mean = sum(e_ms) / len(e_ms)
+    tflops = flop / (e_mean * 1e-3) / 1e12
+    res = {
+        "metric": "token-level block energy TFLOP/s (dense Q K^T twice per row); energy-driven "
+                  "selection ms; retained mass",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "higher_is_better": True,
+        "n_gpus": 1, "steps": args.steps, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "lq": w.lq,
+                   "lk": w.lk, "head_dim": w.head_dim, "rows": rows, "n_k_blocks": nkb,
+                   "tau": tau},
+        "energy_ms": round(e_mean, 4),
+        "energy_ms_p10_p50_p90": [round(x, 4) for x in percentiles(e_ms)],
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "block_energy_bf16_kernel",
+                     "per_launch_flop": flop},
+        "select_energy_ms": round(sum(s_ms) / len(s_ms), 4),
+        "retained_mass_ms": round(sum(m_ms) / len(m_ms), 4),
+        "token_mask": {"nnz": nnz_tok, "density": round(nnz_tok / (rows * nkb), 5),
+                       "mean_retained_mass": round(float(mass_tok.mean()), 5)},
+        "pooled_mask": {"mode": w.mode, "param": w.param, "nnz": nnz_pool,
+                        "density": round(nnz_pool / (rows * nkb), 5),
+                        "mean_retained_mass": round(float(mass_pooled.mean()), 5),
+                        "min_retained_mass": round(float(mass_pooled.min()), 5)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = energy_cpu_baseline(w, q, k, flop, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def energy_cpu_baseline(w, q, k, flop, budget_s):
+    """The oracle's Eq. (5) on as many rows of one head as fit in the budget, extrapolated."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    h = w.heads // 2
+    qh = q[:, h:h + 1].float().cpu().numpy()
+    kh = k[:, h:h + 1].float().cpu().numpy()
+    n, t = 0, 0.0
+    for i in np.random.default_rng(7).permutation(w.n_q_blocks):
+        t0 = time.perf_counter()
+        oracle.block_energy_rows(qh, kh, rows=[int(i)])
+        t += time.perf_counter() - t0
+        n += 1
+        if t >= budget_s and n >= 2:
+            break
+    total_s = t * w.rows / n
+    return {"value": flop / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle: Eq. (5) for {n} query blocks of 1 head ({t:.2f} s), "
+                      f"extrapolated x{w.rows / n:.0f} to all rows ({total_s:.0f} s)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -181,6 +279,8 @@ def main():
         torch.cuda.set_device(0)
         print(json.dumps({"copy_GBps": round(copy_ceiling(torch, torch.device("cuda:0")), 1)}))
         return
+    if args.suite == "energy":
+        return energy_suite(args, torch)
     import dynamic_block_sparse_pool_amd as dbsp
     from synth import BENCH_WORKLOAD, WORKLOADS, make_qkv
 
