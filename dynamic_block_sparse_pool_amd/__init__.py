@@ -24,6 +24,7 @@ from ._abi import DBSP_BLOCK, DbspError
 
 __all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "topk_budget", "select_nnz_bound",
            "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
+           "MaskVote",
            "DbspError", "DBSP_BLOCK", "version"]
 
 
@@ -279,3 +280,44 @@ def select_energy(energy: torch.Tensor, mass: float, text_blocks=(0, 0),
                                 _stream(energy.device))
     _abi.check(st, "dbsp_select_energy")
     return BlockIndex(row_ptr, col_idx, dims.lq // DBSP_BLOCK, nkb, None)
+
+
+class MaskVote:
+    """Cross-input vote of block masks of one shape: add() each calibration input's mask (a
+    BlockIndex), then select(rho) keeps the blocks chosen by at least a fraction rho of them
+    (exact rational comparison) as one static CSR."""
+
+    def __init__(self, batch: int, heads: int, n_q_blocks: int, n_k_blocks: int,
+                 device: torch.device):
+        self.dims = _abi.Dims(batch, heads, n_q_blocks * DBSP_BLOCK, n_k_blocks * DBSP_BLOCK, 128,
+                              _abi.DBSP_BF16)
+        self.rows = batch * heads * n_q_blocks
+        self.n_k_blocks = n_k_blocks
+        self.n_q_blocks = n_q_blocks
+        self.device = torch.device(device)
+        self.counts = torch.zeros((self.rows, n_k_blocks), dtype=torch.int32, device=self.device)
+        self.n_inputs = 0
+
+    def add(self, index: BlockIndex) -> None:
+        if index.row_ptr.numel() != self.rows + 1 or index.n_k_blocks != self.n_k_blocks:
+            raise ValueError("mask shape differs from the vote's")
+        st = _abi.load().dbsp_vote_accumulate(_ptr(index.row_ptr), _ptr(index.col_idx),
+                                              index.col_idx.numel(), ctypes.byref(self.dims),
+                                              _ptr(self.counts), _stream(self.device))
+        _abi.check(st, "dbsp_vote_accumulate")
+        self.n_inputs += 1
+
+    def select(self, rho: float) -> BlockIndex:
+        lib = _abi.load()
+        ws_n = ctypes.c_uint64()
+        _abi.check(lib.dbsp_vote_workspace_bytes(ctypes.byref(self.dims), ctypes.byref(ws_n)),
+                   "dbsp_vote_workspace_bytes")
+        ws = torch.empty(max(ws_n.value, 1), dtype=torch.uint8, device=self.device)
+        row_ptr = torch.empty(self.rows + 1, dtype=torch.int32, device=self.device)
+        col_idx = torch.empty(max(self.rows * self.n_k_blocks, 1), dtype=torch.int32,
+                              device=self.device)
+        st = lib.dbsp_vote_select(_ptr(self.counts), ctypes.byref(self.dims), self.n_inputs,
+                                  float(rho), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                  _ptr(ws), ws.numel(), _stream(self.device))
+        _abi.check(st, "dbsp_vote_select")
+        return BlockIndex(row_ptr, col_idx, self.n_q_blocks, self.n_k_blocks, None)

@@ -54,6 +54,9 @@ SIGNATURES = {
     "dbsp_select_energy": (_i32, [_vp, _PDims, Range, Range, _f64, _vp, _vp, _i64, _vp, _u64,
                                   _vp]),
     "dbsp_select_energy_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
+    "dbsp_vote_accumulate": (_i32, [_vp, _vp, _i64, _PDims, _vp, _vp]),
+    "dbsp_vote_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
+    "dbsp_vote_select": (_i32, [_vp, _PDims, _i32, _f64, _vp, _vp, _i64, _vp, _u64, _vp]),
 }
 
 _lib = None

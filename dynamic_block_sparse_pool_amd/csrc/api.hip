@@ -354,4 +354,51 @@ int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_rang
   return DBSP_OK;
 }
 
+int32_t dbsp_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                             const dbsp_dims* dims, int32_t* counts, void* stream) {
+  if (!shape_ok(dims) || !row_ptr || !counts) return DBSP_ERR_INVALID_ARG;
+  if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
+  if (dbsp::launch_vote_accumulate(row_ptr, col_idx, col_capacity, dims->lk / DBSP_BLOCK,
+                                   rows_of(dims), counts, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_vote_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes) {
+  if (!shape_ok(dims) || !bytes) return DBSP_ERR_INVALID_ARG;
+  *bytes = energy_select_layout(dims).total;
+  return DBSP_OK;
+}
+
+int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n_inputs, double rho,
+                         int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                         void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (!shape_ok(dims) || !counts || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
+  if (n_inputs < 1 || !(rho >= 0.0 && rho <= 1.0)) return DBSP_ERR_INVALID_ARG;  // rejects NaN
+  const int32_t nkb = dims->lk / DBSP_BLOCK;
+  if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  const int64_t bound = rows_of(dims) * (int64_t)nkb;
+  if (bound > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  if (col_capacity < bound) return DBSP_ERR_CAPACITY;
+  const WorkspaceLayout wl = energy_select_layout(dims);
+  if (!workspace || workspace_bytes < wl.total || ((uintptr_t)workspace & 255u))
+    return DBSP_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  dbsp::SelectArgs a{};
+  a.nqb = dims->lq / DBSP_BLOCK;
+  a.nkb = nkb;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.col_capacity = col_capacity;
+  a.counts = reinterpret_cast<int32_t*>(ws + wl.counts);
+  a.masks = reinterpret_cast<uint64_t*>(ws + wl.masks);
+  a.words = (nkb + 63) / 64;
+  a.n_rows = rows_of(dims);
+  if (dbsp::launch_vote_select(counts, n_inputs, rho, a, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
 }  // extern "C"

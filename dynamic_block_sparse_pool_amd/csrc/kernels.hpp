@@ -65,5 +65,12 @@ hipError_t launch_retained_mass(const float* energy, const int32_t* row_ptr,
                                 const int32_t* col_idx, int64_t col_capacity, int nkb,
                                 int64_t rows, double* mass, hipStream_t stream);
 hipError_t launch_select_energy(const SelectArgs& a, const float* energy, hipStream_t stream);
+// row_ptr / col_idx from the per-row counts and kept bitmasks in a.counts / a.masks
+hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream);
+hipError_t launch_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx,
+                                  int64_t col_capacity, int nkb, int64_t rows, int32_t* counts,
+                                  hipStream_t stream);
+hipError_t launch_vote_select(const int32_t* counts, int n_inputs, double rho, const SelectArgs& a,
+                              hipStream_t stream);
 
 }  // namespace dbsp

@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const 
   select_mass_probs<S>(a, p, row, lane);
 }
 
-static hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream) {
+hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream) {
   scan_counts_kernel<<<1, 1024, 0, stream>>>(a.counts, a.row_ptr, a.n_rows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

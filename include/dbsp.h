@@ -13,6 +13,8 @@
  *   dbsp_block_energy     Q, K -> the token-level energy of every (query block, key block) pair.
  *   dbsp_retained_mass    energy, CSR -> the attention mass each row's mask keeps.
  *   dbsp_select_energy    energy -> a CSR by the cumulative-mass rule on token-level energies.
+ *   dbsp_vote_accumulate, dbsp_vote_select
+ *                         masks of several calibration inputs -> one static CSR by vote.
  *
  * What the calls compute follows two pages:
  *   [SparSTAR] "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis", in the
@@ -225,6 +227,31 @@ int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_rang
 
 /* Workspace bytes dbsp_select_energy needs for dims (per-row counts and kept bitmasks). */
 int32_t dbsp_select_energy_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
+
+/*
+ * Cross-input vote ([CalibAtt] key design 2, Eq. (8) and the description of Eq. (9)): the masks
+ * chosen for each calibration input are averaged element-wise and a block is kept when its keep
+ * frequency is at least rho; the result is one static CSR reused for new inputs (key design 4).
+ *
+ * dbsp_vote_accumulate adds one input's mask: counts[r][c] += 1 for every in-range entry c of
+ * CSR row r (row_ptr / col_idx / col_capacity as for dbsp_sparse_attn_fwd; entries of a row
+ * must be distinct, as every CSR this library writes is). counts: device int32 [rows, lk / 128],
+ * zero-filled by the caller before the first input. Calls on one counts buffer must not overlap.
+ *
+ * dbsp_vote_select writes the CSR of {(r, c) : counts[r][c] / n_inputs >= rho}, the comparison
+ * exact on the rational count / n_inputs against the double rho, in [0, 1]; rows ascending as
+ * in dbsp_sparse_select step 5. The nnz bound is rows * (lk / 128); workspace: at least
+ * dbsp_vote_workspace_bytes bytes, 256-byte aligned. The page's worked example: rho = 0.5 with
+ * 64 inputs keeps the blocks counted 32 times or more.
+ * Errors: DBSP_ERR_INVALID_ARG for null pointers, a bad shape, n_inputs < 1 or rho outside
+ * [0, 1]; DBSP_ERR_CAPACITY, DBSP_ERR_WORKSPACE and DBSP_ERR_UNSUPPORTED as dbsp_select_energy.
+ */
+int32_t dbsp_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                             const dbsp_dims* dims, int32_t* counts, void* stream);
+int32_t dbsp_vote_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
+int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n_inputs, double rho,
+                         int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                         void* workspace, uint64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -216,3 +216,29 @@ def test_attn_rejects_too_many_bf16_key_blocks(lib):
     dims = _abi.Dims(1, 1, 128, 65536 * 128, 128, E.DBSP_BF16)
     assert lib.dbsp_sparse_attn_fwd(FAKE, FAKE, FAKE, ctypes.byref(dims), FAKE, FAKE, 16, 0.0, FAKE,
                                     E.DBSP_F32, None, None) == E.DBSP_ERR_UNSUPPORTED
+
+
+def test_vote_calls_reject_bad_arguments(lib):
+    E = _abi
+    good = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_BF16)
+
+    def acc(dims=good, rp=FAKE, ci=FAKE, cap=16, counts=FAKE):
+        return lib.dbsp_vote_accumulate(rp, ci, cap, ctypes.byref(dims), counts, None)
+
+    for kw in ({"rp": None}, {"counts": None}, {"cap": -1}, {"ci": None},
+               {"dims": _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)}):
+        assert acc(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+
+    def sel(dims=good, counts=FAKE, n=4, rho=0.5, rp=FAKE, ci=FAKE, cap=1 << 40, ws=FAKE,
+            ws_bytes=1 << 40):
+        return lib.dbsp_vote_select(counts, ctypes.byref(dims), n, rho, rp, ci, cap, ws, ws_bytes,
+                                    None)
+
+    for kw in ({"counts": None}, {"rp": None}, {"ci": None}, {"n": 0}, {"rho": -0.1},
+               {"rho": 1.5}, {"rho": float("nan")}):
+        assert sel(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    assert sel(cap=31) == E.DBSP_ERR_CAPACITY      # 4 rows x 8 key blocks
+    assert sel(ws=None) == E.DBSP_ERR_WORKSPACE
+    assert sel(ws=ctypes.c_void_p((1 << 20) + 16)) == E.DBSP_ERR_WORKSPACE
+    ws = ctypes.c_uint64()
+    assert lib.dbsp_vote_workspace_bytes(ctypes.byref(good), ctypes.byref(ws)) == 0 and ws.value > 0
