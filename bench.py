@@ -62,9 +62,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
-    ap.add_argument("--suite", choices=("hot", "energy"), default="hot",
+    ap.add_argument("--suite", choices=("hot", "energy", "calibrate"), default="hot",
                     help="hot: the selection + attention step (default); energy: the token-level "
-                         "block energy, energy-driven selection and retained mass (one JSON line)")
+                         "block energy, energy-driven selection and retained mass; calibrate: "
+                         "per-input token-level masks voted into one static CSR, reused on a "
+                         "held-out input (one JSON line each)")
+    ap.add_argument("--inputs", type=int, default=16, help="calibrate: calibration inputs")
     ap.add_argument("--only-copy", action="store_true",
                     help="run only the 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--cold-iters", type=int, default=8,
@@ -240,6 +243,83 @@ def energy_suite(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def calibrate_suite(args, torch):
+    """The offline calibration path: for each of N seeded synthetic inputs, token-level energies
+    -> a mask at tau -> added to the vote; the vote at rho gives one static CSR, which then
+    drives the sparse attention of a held-out input. Reports the per-stage times and how much
+    of the held-out input's token-level attention mass the static mask keeps, next to the mask
+    chosen on that input itself."""
+    import dynamic_block_sparse_pool_amd as dbsp
+    from synth import PROMPT_SHARED, WORKLOADS, make_prompt_qkv
+
+    w = WORKLOADS[args.workload or "star_mid_clip2"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tau, rho, n = 0.9, 0.5, args.inputs
+    rows, nkb = w.rows, w.n_k_blocks
+    vote = dbsp.MaskVote(w.batch, w.heads, w.n_q_blocks, nkb, dev)
+    energy = torch.empty((rows, nkb), dtype=torch.float32, device=dev)
+    t_e, t_s, t_a = [], [], []
+    for p in range(n):
+        q, k, _ = make_prompt_qkv(w, p, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        dbsp.block_energy(q, k, out=energy)
+        ev[1].record()
+        idx = dbsp.select_energy(energy, tau, w.text, w.extra, batch=w.batch, heads=w.heads)
+        ev[2].record()
+        vote.add(idx)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if p > 0:  # the first input warms up
+            t_e.append(ev[0].elapsed_time(ev[1]))
+            t_s.append(ev[1].elapsed_time(ev[2]))
+            t_a.append(ev[2].elapsed_time(ev[3]))
+        del q, k
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    static = vote.select(rho)
+    e1.record()
+    torch.cuda.synchronize()
+    t_vote = e0.elapsed_time(e1)
+    # held-out input: the static mask against its own token-level mask
+    q, k, v = make_prompt_qkv(w, n + 1000, device=dev)
+    dbsp.block_energy(q, k, out=energy)
+    own = dbsp.select_energy(energy, tau, w.text, w.extra, batch=w.batch, heads=w.heads)
+    m_static = dbsp.retained_mass(energy, static, batch=w.batch, heads=w.heads)
+    m_own = dbsp.retained_mass(energy, own, batch=w.batch, heads=w.heads)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    dbsp.sparse_attn_fwd(q, k, v, static, out=out)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(5):
+        dbsp.sparse_attn_fwd(q, k, v, static, out=out)
+    a1.record()
+    torch.cuda.synchronize()
+    nnz_s, nnz_o = static.nnz(), own.nnz()
+    mean = lambda xs: sum(xs) / max(len(xs), 1)
+    res = {
+        "metric": "calibration: per-input energy + selection + vote ms; static-mask density and "
+                  "retained mass on a held-out input",
+        "value": round(mean(t_e) + mean(t_s) + mean(t_a), 4), "unit": "ms per calibration input",
+        "higher_is_better": False, "n_gpus": 1, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "lq": w.lq, "lk": w.lk, "rows": rows,
+                   "n_k_blocks": nkb, "inputs": n, "tau": tau, "rho": rho,
+                   "prompt_shared_variance": PROMPT_SHARED},
+        "energy_ms": round(mean(t_e), 4), "select_energy_ms": round(mean(t_s), 4),
+        "vote_accumulate_ms": round(mean(t_a), 4), "vote_select_ms": round(t_vote, 4),
+        "static_mask": {"nnz": nnz_s, "density": round(nnz_s / (rows * nkb), 5),
+                        "heldout_mean_retained_mass": round(float(m_static.mean()), 5),
+                        "heldout_min_retained_mass": round(float(m_static.min()), 5),
+                        "attn_ms": round(a0.elapsed_time(a1) / 5, 4)},
+        "heldout_own_mask": {"nnz": nnz_o, "density": round(nnz_o / (rows * nkb), 5),
+                             "mean_retained_mass": round(float(m_own.mean()), 5)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def energy_cpu_baseline(w, q, k, flop, budget_s):
     """The oracle's Eq. (5) on as many rows of one head as fit in the budget, extrapolated."""
     import numpy as np
@@ -281,6 +361,8 @@ def main():
         return
     if args.suite == "energy":
         return energy_suite(args, torch)
+    if args.suite == "calibrate":
+        return calibrate_suite(args, torch)
     import dynamic_block_sparse_pool_amd as dbsp
     from synth import BENCH_WORKLOAD, WORKLOADS, make_qkv
 

@@ -129,6 +129,39 @@ def make_qkv(w: Workload, device="cpu", seed: int = 0, heads: Optional[int] = No
     return tuple(make_tensor(w, t, device, seed, heads) for t in ("q", "k", "v"))
 
 
+PROMPT_SHARED = 0.75  # share of the centroid variance common to every calibration prompt
+
+
+def make_prompt_tensor(w: Workload, tensor: str, prompt: int, device="cpu",
+                       shared: float = PROMPT_SHARED) -> torch.Tensor:
+    """Q, K or V of one synthetic calibration "prompt" of a centroid workload. The centroid of
+    every (tensor, batch, head, block) is sqrt(shared) * a + sqrt(1 - shared) * b with a drawn
+    once for the workload (common to all prompts) and b per prompt, both N(0, 2^2 I_d), so the
+    centroid keeps the N(0, 2^2 I_d) law of make_tensor while prompts of one head share most of
+    their block structure; tokens add per-prompt N(0, 0.5^2 I_d) noise."""
+    if w.structure != "centroid":
+        raise ValueError("prompts are defined for centroid workloads")
+    length = w.lq if tensor == "q" else w.lk
+    nb, d = length // BLOCK, w.head_dim
+    dev = torch.device(device)
+    g_common = torch.Generator(device=dev)
+    g_common.manual_seed(_seed(0x5EED, w.wid, tensor))
+    g_prompt = torch.Generator(device=dev)
+    g_prompt.manual_seed(_seed(0x1000 + prompt, w.wid, tensor))
+    cent = torch.randn((w.batch, w.heads, nb, 1, d), generator=g_common, device=dev,
+                       dtype=torch.float32).mul_(2.0 * shared ** 0.5)
+    cent.add_(torch.randn((w.batch, w.heads, nb, 1, d), generator=g_prompt, device=dev,
+                          dtype=torch.float32), alpha=2.0 * (1.0 - shared) ** 0.5)
+    x = torch.randn((w.batch, w.heads, nb, BLOCK, d), generator=g_prompt, device=dev,
+                    dtype=torch.float32)
+    x.mul_(0.5).add_(cent)
+    return x.view(w.batch, w.heads, length, d).to(w.torch_dtype).contiguous()
+
+
+def make_prompt_qkv(w: Workload, prompt: int, device="cpu", shared: float = PROMPT_SHARED):
+    return tuple(make_prompt_tensor(w, t, prompt, device, shared) for t in ("q", "k", "v"))
+
+
 def small_variants():
     """Reduced shapes for parity tests the oracle finishes in seconds.
 
