@@ -13,6 +13,7 @@ What it computes, step by step, in the order the pages describe:
                 (two independent formulations), and the dense reference
   energy.py     token-level block energy (CalibAtt Eq. (5)) and retained mass of a mask
   vote.py       cross-input vote of binary masks (CalibAtt Eq. (8)/(9))
+  anchor.py     the anchor-row path of spatially repeating heads (CalibAtt key designs 3, 4)
 
 Every function cites the passage it follows by page title and section. Readings taken where the
 pages are silent are listed in the docstrings of the functions that make them.
@@ -23,10 +24,12 @@ from .select import (BLOCK, MASS_BITS, block_scores, block_softmax, forced_block
 from .attention import attention_dense, attention_masked, attention_rows
 from .energy import block_energy_rows, retained_mass, token_upper_bound
 from .vote import vote_masks
+from .anchor import anchor_attention, anchor_rows, nearest_anchor
 
 __all__ = [
     "BLOCK", "MASS_BITS", "n_blocks", "pool", "block_scores", "block_softmax", "forced_blocks",
     "topk_budget", "select_topk", "mass_units", "mass_threshold_units", "select_mass", "to_csr",
     "sparse_select", "attention_rows", "attention_masked", "attention_dense", "block_energy_rows",
-    "token_upper_bound", "retained_mass", "vote_masks",
+    "token_upper_bound", "retained_mass", "vote_masks", "anchor_rows", "nearest_anchor",
+    "anchor_attention",
 ]

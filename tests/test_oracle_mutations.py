@@ -9,6 +9,7 @@ import pytest
 import oracle
 import oracle.attention as oatt
 import oracle.energy as oen
+import oracle.anchor as oanc
 import oracle.select as osel
 from tests import test_oracle_pins as pins
 
@@ -81,6 +82,17 @@ def _upper_bound_off_by_one(q, k, rows, budgets, scale=None, block=oracle.BLOCK)
     return oen._orig_token_upper_bound(q, k, rows, [max(m - 1, 0) for m in budgets], scale, block)
 
 
+def _anchors_from_zero(rows_per_frame, n_anchors):
+    # equally spaced starting at row 0 instead of band centres
+    return np.array([(j * rows_per_frame) // n_anchors for j in range(n_anchors)], dtype=np.int64)
+
+
+def _nearest_ties_high(rows_per_frame, n_anchors):
+    a = oanc.anchor_rows(rows_per_frame, n_anchors)
+    return np.array([max(range(a.size), key=lambda j: (-abs(r - a[j]), j))
+                     for r in range(rows_per_frame)], dtype=np.int64)
+
+
 def _softmax_weighted_unnormalised(logits, values):
     m = logits.max(axis=-1, keepdims=True)
     e = np.exp(logits - m)
@@ -107,6 +119,10 @@ MUTATIONS = {
     "upper bound from the smallest probabilities": (
         oen, "token_upper_bound", _upper_bound_smallest,
         [pins.test_token_upper_bound_brute_force_and_bounds]),
+    "anchors start at row 0": (oanc, "anchor_rows", _anchors_from_zero,
+                               [pins.test_anchor_rows_are_band_centres]),
+    "nearest anchor ties high": (oanc, "nearest_anchor", _nearest_ties_high,
+                                 [pins.test_anchor_rows_are_band_centres]),
     "upper bound one token short": (oen, "token_upper_bound", _upper_bound_off_by_one,
                                     [pins.test_token_upper_bound_brute_force_and_bounds,
                                      pins.test_token_upper_bound_mean_field_equals_block_topk]),

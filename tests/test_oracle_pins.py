@@ -473,3 +473,65 @@ def test_vote_worked_example():
     for j, c in enumerate(counts):
         masks[:c, j] = True
     assert oracle.vote_masks(masks, g["rho"]).tolist() == g["kept"]
+
+
+# ---------------------------------------------------------------- anchor rows (repeating heads)
+
+def test_anchor_rows_are_band_centres():
+    # the page's default of 5 anchors on the 45 rows of a Wan 720p latent frame
+    assert oracle.anchor_rows(45, 5).tolist() == [4, 13, 22, 31, 40]
+    assert oracle.anchor_rows(7, 7).tolist() == list(range(7))
+    assert oracle.anchor_rows(10, 1).tolist() == [5]
+    near = oracle.nearest_anchor(45, 5)
+    # bands of 9 rows map to their centre; every row is at most 4 rows from its anchor
+    assert near.tolist() == [r // 9 for r in range(45)]
+    assert oracle.anchor_rows(6, 2).tolist() == [1, 4]
+    assert oracle.nearest_anchor(6, 2).tolist() == [0, 0, 0, 1, 1, 1]
+    # ties go to the lower anchor: anchors at rows 2 and 6 of 8, row 4 is 2 away from both
+    assert oracle.anchor_rows(8, 2).tolist() == [2, 6]
+    assert oracle.nearest_anchor(8, 2).tolist() == [0, 0, 0, 0, 0, 1, 1, 1]
+
+
+def _dense(q, k, v):
+    return oracle.attention_dense(q, k, v)
+
+
+def test_anchor_path_reduces_to_dense():
+    rng = np.random.default_rng(31)
+    b, h, frames, rows, width, d = 1, 2, 2, 4, 16, 8
+    lq = frames * rows * width + 20                      # a trailing partial block
+    q = rng.standard_normal((b, h, lq, d))
+    k = rng.standard_normal((b, h, 96, d))
+    v = rng.standard_normal((b, h, 96, d))
+    o_d, l_d = _dense(q, k, v)
+    # every row its own anchor: exactly dense attention
+    o, l = oracle.anchor_attention(q, k, v, frames, rows, width, rows)
+    np.testing.assert_allclose(o, o_d, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, l_d, rtol=1e-12, atol=1e-12)
+    # fewer anchors: anchor rows and the tail are dense; other rows copy their anchor's row
+    o, l = oracle.anchor_attention(q, k, v, frames, rows, width, 2)
+    a = oracle.anchor_rows(rows, 2)
+    near = oracle.nearest_anchor(rows, 2)
+    for f in range(frames):
+        for r in range(rows):
+            t = f * rows * width + r * width
+            src = f * rows * width + a[near[r]] * width
+            np.testing.assert_allclose(o[:, :, t:t + width], o_d[:, :, src:src + width],
+                                       rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o[:, :, frames * rows * width:], o_d[:, :, frames * rows * width:],
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_anchor_path_exact_on_repeating_rows():
+    # a perfectly repeating head: every spatial row of a frame has the same queries, so the
+    # broadcast loses nothing and the anchor path equals dense attention
+    rng = np.random.default_rng(37)
+    frames, rows, width, d = 3, 6, 8, 16
+    row_q = rng.standard_normal((frames, 1, width, d))
+    q = np.broadcast_to(row_q, (frames, rows, width, d)).reshape(1, 1, -1, d).copy()
+    k = rng.standard_normal((1, 1, 64, d))
+    v = rng.standard_normal((1, 1, 64, d))
+    o, l = oracle.anchor_attention(q, k, v, frames, rows, width, 2)
+    o_d, l_d = _dense(q, k, v)
+    np.testing.assert_allclose(o, o_d, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, l_d, rtol=1e-12, atol=1e-12)
