@@ -24,7 +24,7 @@ from ._abi import DBSP_BLOCK, DbspError
 
 __all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "topk_budget", "select_nnz_bound",
            "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
-           "MaskVote",
+           "MaskVote", "anchor_attn_fwd",
            "DbspError", "DBSP_BLOCK", "version"]
 
 
@@ -321,3 +321,36 @@ class MaskVote:
                                   _ptr(ws), ws.numel(), _stream(self.device))
         _abi.check(st, "dbsp_vote_select")
         return BlockIndex(row_ptr, col_idx, self.n_q_blocks, self.n_k_blocks, None)
+
+
+def anchor_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, frames: int,
+                    rows_per_frame: int, row_width: int, n_anchors: int = 5,
+                    softmax_scale: float = 0.0, out_dtype: Optional[torch.dtype] = None,
+                    return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Attention of a spatially repeating head: only n_anchors equally spaced rows per frame
+    attend (to all keys); every spatial row takes its nearest anchor row's output. Tokens after
+    the last frame attend as themselves. Returns O (and lse if return_lse)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t)
+    dims = _dims(q, k)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    odt = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
+    if out is None:
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    lib = _abi.load()
+    n = ctypes.c_uint64()
+    geom = (int(frames), int(rows_per_frame), int(row_width), int(n_anchors))
+    _abi.check(lib.dbsp_anchor_workspace_bytes(ctypes.byref(dims), *geom, _dtype_code(out),
+                                               ctypes.byref(n)), "dbsp_anchor_workspace_bytes")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    st = lib.dbsp_anchor_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), *geom,
+                                  float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
+                                  _ptr(workspace), workspace.numel(), _stream(q.device))
+    _abi.check(st, "dbsp_anchor_attn_fwd")
+    return (out, lse) if return_lse else out

@@ -122,6 +122,48 @@ WorkspaceLayout layout_of(const dbsp_dims* d, int32_t mode) {
   return w;
 }
 
+// Anchor-row path: validated geometry and workspace layout.
+struct AnchorLayout {
+  dbsp::AnchorGeom g;
+  uint64_t qa, oa, lse_a, row_ptr, col_idx, total;
+};
+
+int32_t anchor_layout(const dbsp_dims* d, int32_t frames, int32_t rows, int32_t width,
+                      int32_t n_anchors, int32_t o_dtype, AnchorLayout* out) {
+  if (!shape_ok(d) || frames < 1 || rows < 1 || width < 1 || n_anchors < 1 || n_anchors > rows)
+    return DBSP_ERR_INVALID_ARG;
+  if (o_dtype != DBSP_F32 && o_dtype != DBSP_BF16) return DBSP_ERR_INVALID_ARG;
+  const int64_t video = (int64_t)frames * rows * width;
+  if (video > d->lq) return DBSP_ERR_INVALID_ARG;
+  AnchorLayout l{};
+  l.g.frames = frames;
+  l.g.rows = rows;
+  l.g.width = width;
+  l.g.n_anchors = n_anchors;
+  l.g.lq = d->lq;
+  l.g.la = (int64_t)frames * n_anchors * width + (d->lq - video);
+  l.g.la_pad = (l.g.la + DBSP_BLOCK - 1) / DBSP_BLOCK * DBSP_BLOCK;
+  const uint64_t bh = (uint64_t)d->batch * d->heads;
+  const uint64_t in_elt = d->dtype == DBSP_BF16 ? 2 : 4, out_elt = o_dtype == DBSP_BF16 ? 2 : 4;
+  const uint64_t rows_a = bh * (uint64_t)(l.g.la_pad / DBSP_BLOCK);
+  const uint64_t nkb = d->lk / DBSP_BLOCK;
+  if (rows_a * nkb > (uint64_t)INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  uint64_t off = 0;
+  l.qa = off;
+  off = align256(off + bh * l.g.la_pad * d->head_dim * in_elt);
+  l.oa = off;
+  off = align256(off + bh * l.g.la_pad * d->head_dim * out_elt);
+  l.lse_a = off;
+  off = align256(off + bh * l.g.la_pad * sizeof(float));
+  l.row_ptr = off;
+  off = align256(off + (rows_a + 1) * sizeof(int32_t));
+  l.col_idx = off;
+  off = align256(off + rows_a * nkb * sizeof(int32_t));
+  l.total = off;
+  *out = l;
+  return DBSP_OK;
+}
+
 // dbsp_select_energy: per-row counts and kept bitmasks only.
 WorkspaceLayout energy_select_layout(const dbsp_dims* d) {
   WorkspaceLayout w{};
@@ -397,6 +439,60 @@ int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n
   a.n_rows = rows_of(dims);
   if (dbsp::launch_vote_select(counts, n_inputs, rho, a, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_anchor_workspace_bytes(const dbsp_dims* dims, int32_t frames, int32_t rows_per_frame,
+                                    int32_t row_width, int32_t n_anchors, int32_t o_dtype,
+                                    uint64_t* bytes) {
+  if (!bytes) return DBSP_ERR_INVALID_ARG;
+  AnchorLayout l;
+  const int32_t st = anchor_layout(dims, frames, rows_per_frame, row_width, n_anchors, o_dtype, &l);
+  if (st != DBSP_OK) return st;
+  *bytes = l.total;
+  return DBSP_OK;
+}
+
+int32_t dbsp_anchor_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
+                             int32_t frames, int32_t rows_per_frame, int32_t row_width,
+                             int32_t n_anchors, float softmax_scale, void* o, int32_t o_dtype,
+                             float* lse_out, void* workspace, uint64_t workspace_bytes,
+                             void* stream) {
+  if (!shape_ok(dims) || !q || !k || !v || !o) return DBSP_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      ((uintptr_t)lse_out & 3u))
+    return DBSP_ERR_INVALID_ARG;
+  if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
+  AnchorLayout l;
+  const int32_t st = anchor_layout(dims, frames, rows_per_frame, row_width, n_anchors, o_dtype, &l);
+  if (st != DBSP_OK) return st;
+  if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
+  if (dims->dtype == DBSP_BF16 && dims->lk / DBSP_BLOCK > kMaxBf16KeyBlocks)
+    return DBSP_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255u))
+    return DBSP_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale
+                                          : (float)(1.0 / sqrt((double)dims->head_dim));
+  char* ws = static_cast<char*>(workspace);
+  dbsp::AnchorArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qa = ws + l.qa;
+  a.oa = ws + l.oa;
+  a.lse_a = reinterpret_cast<float*>(ws + l.lse_a);
+  a.row_ptr = reinterpret_cast<int32_t*>(ws + l.row_ptr);
+  a.col_idx = reinterpret_cast<int32_t*>(ws + l.col_idx);
+  a.bh = (int64_t)dims->batch * dims->heads;
+  a.nkb = dims->lk / DBSP_BLOCK;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o;
+  a.o_bf16 = o_dtype == DBSP_BF16;
+  a.lse = lse_out;
+  a.geom = l.g;
+  if (dbsp::launch_anchor(a, dims->head_dim, dims->dtype == DBSP_BF16,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
     return DBSP_ERR_HIP;
   return DBSP_OK;
 }

@@ -54,6 +54,32 @@ struct EnergyArgs {
   float* lse;        // nullable [rows * 128]
 };
 
+// Query geometry of the anchor-row path: frames x rows x width tokens, then trailing tokens.
+struct AnchorGeom {
+  int frames, rows, width, n_anchors;
+  int64_t lq;      // query tokens per (batch, head)
+  int64_t la;      // packed queries: frames * n_anchors * width + (lq - frames * rows * width)
+  int64_t la_pad;  // la rounded up to a block multiple
+};
+
+struct AnchorArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* qa;          // workspace: packed queries [bh, la_pad, d], input dtype
+  void* oa;          // workspace: packed outputs [bh, la_pad, d], output dtype
+  float* lse_a;      // workspace: [bh, la_pad]
+  int32_t* row_ptr;  // workspace: dense CSR over the packed query blocks
+  int32_t* col_idx;
+  int64_t bh;
+  int nkb;
+  float scale_log2;
+  void* o;
+  int o_bf16;
+  float* lse;        // nullable [bh, lq]
+  AnchorGeom geom;
+};
+
 hipError_t launch_pool(const void* q, const void* k, uint16_t* qsplit, uint16_t* ksplit,
                        int64_t nq_blocks, int64_t nk_blocks, int nkb, int head_dim, bool bf16,
                        hipStream_t stream);
@@ -70,6 +96,7 @@ hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx,
                                   int64_t col_capacity, int nkb, int64_t rows, int32_t* counts,
                                   hipStream_t stream);
+hipError_t launch_anchor(const AnchorArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_vote_select(const int32_t* counts, int n_inputs, double rho, const SelectArgs& a,
                               hipStream_t stream);
 

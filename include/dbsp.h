@@ -15,6 +15,8 @@
  *   dbsp_select_energy    energy -> a CSR by the cumulative-mass rule on token-level energies.
  *   dbsp_vote_accumulate, dbsp_vote_select
  *                         masks of several calibration inputs -> one static CSR by vote.
+ *   dbsp_anchor_attn_fwd  the alternative path of spatially repeating heads: attention for a few
+ *                         anchor rows per frame, broadcast to the nearest rows.
  *
  * What the calls compute follows two pages:
  *   [SparSTAR] "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis", in the
@@ -252,6 +254,37 @@ int32_t dbsp_vote_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
 int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n_inputs, double rho,
                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                          void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Anchor-row attention for spatially repeating heads ([CalibAtt] key design 3, spatial
+ * repetition, and key design 4, the repeating-head execution path).
+ *
+ * The query sequence of each (batch, head) is `frames` frames of `rows_per_frame` spatial rows
+ * of `row_width` tokens (token (f, r, c) at f * rows_per_frame * row_width + r * row_width + c),
+ * followed by lq - frames * rows_per_frame * row_width trailing tokens in no frame. Per frame,
+ * the n_anchors anchor rows a_j = floor((2 j + 1) * rows_per_frame / (2 * n_anchors)) attend to
+ * all lk keys (dense softmax attention, arithmetic as dbsp_sparse_attn_fwd); every row r of the
+ * frame takes the output of its nearest anchor row (smallest |r - a_j|, ties to the lower j) at
+ * the same column, bit for bit; trailing tokens attend as themselves. The page's default is 5
+ * anchors per frame (for a Wan 720p latent frame: 45 rows of 80 tokens).
+ *
+ * o: [batch, heads, lq, head_dim] in o_dtype; lse_out (nullable): float32 [batch, heads, lq],
+ * each token's being its anchor's. workspace: at least dbsp_anchor_workspace_bytes for the same
+ * arguments, 256-byte aligned (packed anchor queries and outputs and a dense CSR of the packed
+ * query blocks).
+ * Errors: DBSP_ERR_INVALID_ARG for null or misaligned pointers, a bad shape, frames, rows or
+ * width < 1, n_anchors outside [1, rows_per_frame], a geometry longer than lq or a non-finite
+ * scale; DBSP_ERR_UNSUPPORTED as dbsp_sparse_attn_fwd, or when the packed CSR would exceed
+ * INT32_MAX entries; DBSP_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ */
+int32_t dbsp_anchor_workspace_bytes(const dbsp_dims* dims, int32_t frames, int32_t rows_per_frame,
+                                    int32_t row_width, int32_t n_anchors, int32_t o_dtype,
+                                    uint64_t* bytes);
+int32_t dbsp_anchor_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
+                             int32_t frames, int32_t rows_per_frame, int32_t row_width,
+                             int32_t n_anchors, float softmax_scale, void* o, int32_t o_dtype,
+                             float* lse_out, void* workspace, uint64_t workspace_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }
