@@ -62,11 +62,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
-    ap.add_argument("--suite", choices=("hot", "energy", "calibrate"), default="hot",
+    ap.add_argument("--suite", choices=("hot", "energy", "calibrate", "anchor"), default="hot",
                     help="hot: the selection + attention step (default); energy: the token-level "
                          "block energy, energy-driven selection and retained mass; calibrate: "
                          "per-input token-level masks voted into one static CSR, reused on a "
-                         "held-out input (one JSON line each)")
+                         "held-out input; anchor: the anchor-row path of repeating heads on "
+                         "the DiT geometry (one JSON line each)")
     ap.add_argument("--inputs", type=int, default=16, help="calibrate: calibration inputs")
     ap.add_argument("--only-copy", action="store_true",
                     help="run only the 1 GiB device copy (counter calibration) and exit")
@@ -320,6 +321,59 @@ def calibrate_suite(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def anchor_suite(args, torch):
+    """The anchor-row path on the DiT shape: 21 latent frames of 45 rows x 80 tokens plus 48
+    trailing tokens, 5 anchors per frame, all 40 heads; executed FLOP = packed query blocks x
+    key blocks x 4 * 128^2 * d."""
+    import dynamic_block_sparse_pool_amd as dbsp
+    from synth import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload or "dit_mass"]
+    frames, rows, width, k_anchors = 21, 45, 80, 5
+    if frames * rows * width > w.lq:
+        raise SystemExit("workload shorter than the 21 x 45 x 80 geometry")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_qkv(w, device=dev, seed=args.seed)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    la = frames * k_anchors * width + (w.lq - frames * rows * width)
+    la_pad = -(-la // 128) * 128
+    ws = None
+    for _ in range(max(args.warmup, 1)):
+        dbsp.anchor_attn_fwd(q, k, v, frames, rows, width, k_anchors, out=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        dbsp.anchor_attn_fwd(q, k, v, frames, rows, width, k_anchors, out=out, workspace=ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    mean = sum(ms) / len(ms)
+    pairs = w.batch * w.heads * (la_pad // 128) * w.n_k_blocks
+    flop = pairs * 4 * 128 * 128 * w.head_dim
+    dense_flop = w.rows * w.n_k_blocks * 4 * 128 * 128 * w.head_dim
+    tflops = flop / (mean * 1e-3) / 1e12
+    res = {
+        "metric": "anchor-row attention ms and executed TFLOP/s (repeating heads)",
+        "value": round(mean, 4), "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "lq": w.lq, "lk": w.lk,
+                   "frames": frames, "rows_per_frame": rows, "row_width": width,
+                   "anchors": k_anchors, "packed_queries": la, "packed_padded": la_pad},
+        "ms_p10_p50_p90": [round(x, 4) for x in percentiles(ms)],
+        "executed_TFLOPs": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fwd_bf16_kernel (packed anchor queries)",
+                     "per_launch_flop": flop},
+        "interaction_sparsity": round(1 - k_anchors / rows, 4),
+        "executed_vs_dense_flop": round(flop / dense_flop, 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def energy_cpu_baseline(w, q, k, flop, budget_s):
     """The oracle's Eq. (5) on as many rows of one head as fit in the budget, extrapolated."""
     import numpy as np
@@ -363,6 +417,8 @@ def main():
         return energy_suite(args, torch)
     if args.suite == "calibrate":
         return calibrate_suite(args, torch)
+    if args.suite == "anchor":
+        return anchor_suite(args, torch)
     import dynamic_block_sparse_pool_amd as dbsp
     from synth import BENCH_WORKLOAD, WORKLOADS, make_qkv
 
