@@ -127,9 +127,13 @@ class SelectPlan:
     def __init__(self, q: torch.Tensor, k: torch.Tensor, text_blocks=(0, 0),
                  dense_extra_blocks=(0, 0), density: Optional[float] = None,
                  mass: Optional[float] = None, topk_override: int = -1,
-                 score_scale: float = 0.0, return_scores: bool = False):
+                 score_scale: float = 0.0, return_scores: bool = False,
+                 forced_blocks=None):
         if (density is None) == (mass is None):
             raise ValueError("give exactly one of density (Top-K) or mass (cumulative mass)")
+        # an explicit forced list replaces the two ranges
+        self.forced = (None if forced_blocks is None else
+                       (ctypes.c_int32 * len(forced_blocks))(*[int(c) for c in forced_blocks]))
         _check_device_tensor("q", q)
         _check_device_tensor("k", k)
         self.dims = _dims(q, k)
@@ -142,8 +146,15 @@ class SelectPlan:
         self.device = q.device
         rows = self.dims.batch * self.dims.heads * (self.dims.lq // DBSP_BLOCK)
         nkb = self.dims.lk // DBSP_BLOCK
-        self.capacity = select_nnz_bound(self.dims, self.mode, self.param, text_blocks,
-                                         dense_extra_blocks, self.topk_override)
+        if self.forced is None:
+            self.capacity = select_nnz_bound(self.dims, self.mode, self.param, text_blocks,
+                                             dense_extra_blocks, self.topk_override)
+        else:
+            out = ctypes.c_int64()
+            _abi.check(_abi.load().dbsp_select_nnz_bound_list(
+                ctypes.byref(self.dims), self.mode, self.param, self.forced, len(self.forced),
+                self.topk_override, ctypes.byref(out)), "dbsp_select_nnz_bound_list")
+            self.capacity = out.value
         ws = select_workspace_bytes(self.dims, self.mode)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
         self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
@@ -161,11 +172,18 @@ class SelectPlan:
             raise ValueError("q / k shape or dtype differs from the plan")
         _check_device_tensor("q", q)
         _check_device_tensor("k", k)
-        st = _abi.load().dbsp_sparse_select(
-            _ptr(q), _ptr(k), ctypes.byref(self.dims), self.text, self.extra, self.mode,
-            self.param, self.topk_override, self.score_scale, _ptr(self.row_ptr),
-            _ptr(self.col_idx), self.col_idx.numel(), _ptr(self.scores), _ptr(self.workspace),
-            self.workspace.numel(), _stream(q.device))
+        if self.forced is None:
+            st = _abi.load().dbsp_sparse_select(
+                _ptr(q), _ptr(k), ctypes.byref(self.dims), self.text, self.extra, self.mode,
+                self.param, self.topk_override, self.score_scale, _ptr(self.row_ptr),
+                _ptr(self.col_idx), self.col_idx.numel(), _ptr(self.scores),
+                _ptr(self.workspace), self.workspace.numel(), _stream(q.device))
+        else:
+            st = _abi.load().dbsp_sparse_select_list(
+                _ptr(q), _ptr(k), ctypes.byref(self.dims), self.forced, len(self.forced),
+                self.mode, self.param, self.topk_override, self.score_scale, _ptr(self.row_ptr),
+                _ptr(self.col_idx), self.col_idx.numel(), _ptr(self.scores),
+                _ptr(self.workspace), self.workspace.numel(), _stream(q.device))
         _abi.check(st, "dbsp_sparse_select")
         return self.index
 
@@ -173,12 +191,13 @@ class SelectPlan:
 def sparse_select(q: torch.Tensor, k: torch.Tensor, text_blocks: Tuple[int, int] = (0, 0),
                   dense_extra_blocks: Tuple[int, int] = (0, 0), density: Optional[float] = None,
                   mass: Optional[float] = None, topk_override: int = -1, score_scale: float = 0.0,
-                  return_scores: bool = False) -> BlockIndex:
-    """Pool Q and K per 128-token block, score block pairs per head, keep the forced ranges and
-    pick the remaining key blocks per (head, query block): Top-K at `density`, or the shortest
-    cumulative-mass prefix reaching `mass`. Returns the CSR skip list."""
+                  return_scores: bool = False, forced_blocks=None) -> BlockIndex:
+    """Pool Q and K per 128-token block, score block pairs per head, keep the forced ranges (or
+    the explicit `forced_blocks` list, which replaces them) and pick the remaining key blocks per
+    (head, query block): Top-K at `density`, or the shortest cumulative-mass prefix reaching
+    `mass`. Returns the CSR skip list."""
     plan = SelectPlan(q, k, text_blocks, dense_extra_blocks, density, mass, topk_override,
-                      score_scale, return_scores)
+                      score_scale, return_scores, forced_blocks)
     return plan.run(q, k)
 
 

@@ -47,13 +47,48 @@ int32_t forced_count(int32_t nkb, dbsp_range t, dbsp_range e) {
   return (t.end - t.begin) + (e.end - e.begin);
 }
 
-int32_t topk_k(const dbsp_dims* d, double density, dbsp_range t, dbsp_range e, int32_t override_k,
-               int32_t* k_out, int32_t* forced_out) {
+// The forced key blocks of a call: two ranges, or an explicit list held as a bitmask.
+struct ForcedSet {
+  bool by_words = false;
+  dbsp_range t{0, 0}, e{0, 0};
+  uint64_t words[dbsp::kMaxForcedWords] = {};
+  int32_t count = 0;
+};
+
+int32_t forced_from_ranges(int32_t nkb, dbsp_range t, dbsp_range e, ForcedSet* f) {
+  const int32_t n = forced_count(nkb, t, e);
+  if (n < 0) return DBSP_ERR_INVALID_ARG;
+  f->by_words = false;
+  f->t = t;
+  f->e = e;
+  f->count = n;
+  return DBSP_OK;
+}
+
+// Indices must lie in [0, nkb) and be distinct; nkb above the bitmask size is unsupported.
+int32_t forced_from_list(int32_t nkb, const int32_t* list, int32_t n, ForcedSet* f) {
+  if (n < 0 || (n > 0 && !list)) return DBSP_ERR_INVALID_ARG;
+  if (nkb > 64 * dbsp::kMaxForcedWords) return DBSP_ERR_UNSUPPORTED;
+  ForcedSet r;
+  r.by_words = true;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t c = list[i];
+    if (c < 0 || c >= nkb) return DBSP_ERR_INVALID_ARG;
+    uint64_t& w = r.words[c >> 6];
+    const uint64_t bit = 1ull << (c & 63);
+    if (w & bit) return DBSP_ERR_INVALID_ARG;  // duplicate
+    w |= bit;
+  }
+  r.count = n;
+  *f = r;
+  return DBSP_OK;
+}
+
+int32_t topk_k_f(const dbsp_dims* d, double density, const ForcedSet& fs, int32_t override_k,
+                 int32_t* k_out) {
   if (!shape_ok(d) || !k_out) return DBSP_ERR_INVALID_ARG;
   const int32_t nkb = d->lk / DBSP_BLOCK;
-  const int32_t f = forced_count(nkb, t, e);
-  if (f < 0) return DBSP_ERR_INVALID_ARG;
-  const int32_t ncand = nkb - f;
+  const int32_t ncand = nkb - fs.count;
   int64_t k;
   if (override_k >= 0) {
     if (override_k > ncand) return DBSP_ERR_INVALID_ARG;
@@ -64,28 +99,53 @@ int32_t topk_k(const dbsp_dims* d, double density, dbsp_range t, dbsp_range e, i
     if (k > ncand) k = ncand;
   }
   *k_out = (int32_t)k;
-  if (forced_out) *forced_out = f;
   return DBSP_OK;
 }
 
-int32_t nnz_bound(const dbsp_dims* d, int32_t mode, double param, dbsp_range t, dbsp_range e,
-                  int32_t override_k, int64_t* out) {
+int32_t topk_k(const dbsp_dims* d, double density, dbsp_range t, dbsp_range e, int32_t override_k,
+               int32_t* k_out) {
+  if (!shape_ok(d) || !k_out) return DBSP_ERR_INVALID_ARG;
+  ForcedSet fs;
+  const int32_t st = forced_from_ranges(d->lk / DBSP_BLOCK, t, e, &fs);
+  if (st != DBSP_OK) return st;
+  return topk_k_f(d, density, fs, override_k, k_out);
+}
+
+int32_t nnz_bound_f(const dbsp_dims* d, int32_t mode, double param, const ForcedSet& fs,
+                    int32_t override_k, int64_t* out) {
   if (!shape_ok(d) || !out) return DBSP_ERR_INVALID_ARG;
   const int32_t nkb = d->lk / DBSP_BLOCK;
   if (mode == DBSP_TOPK) {
-    int32_t k, f;
-    int32_t st = topk_k(d, param, t, e, override_k, &k, &f);
+    int32_t k;
+    const int32_t st = topk_k_f(d, param, fs, override_k, &k);
     if (st != DBSP_OK) return st;
-    *out = rows_of(d) * (int64_t)(f + k);
+    *out = rows_of(d) * (int64_t)(fs.count + k);
     return DBSP_OK;
   }
   if (mode == DBSP_MASS) {
-    if (forced_count(nkb, t, e) < 0) return DBSP_ERR_INVALID_ARG;
     if (!(param > 0.0 && param <= 1.0)) return DBSP_ERR_INVALID_ARG;
     *out = rows_of(d) * (int64_t)nkb;
     return DBSP_OK;
   }
   return DBSP_ERR_INVALID_ARG;
+}
+
+int32_t nnz_bound(const dbsp_dims* d, int32_t mode, double param, dbsp_range t, dbsp_range e,
+                  int32_t override_k, int64_t* out) {
+  if (!shape_ok(d) || !out) return DBSP_ERR_INVALID_ARG;
+  ForcedSet fs;
+  const int32_t st = forced_from_ranges(d->lk / DBSP_BLOCK, t, e, &fs);
+  if (st != DBSP_OK) return st;
+  return nnz_bound_f(d, mode, param, fs, override_k, out);
+}
+
+void apply_forced(const ForcedSet& fs, dbsp::SelectArgs* a) {
+  a->t0 = fs.t.begin;
+  a->t1 = fs.t.end;
+  a->e0 = fs.e.begin;
+  a->e1 = fs.e.end;
+  a->forced_by_words = fs.by_words ? 1 : 0;
+  for (int i = 0; i < dbsp::kMaxForcedWords; ++i) a->forced_words[i] = fs.words[i];
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
@@ -196,7 +256,17 @@ const char* dbsp_status_string(int32_t status) {
 
 int32_t dbsp_topk_budget(const dbsp_dims* dims, double density, dbsp_range text_blocks,
                          dbsp_range dense_extra_blocks, int32_t topk_override, int32_t* k_out) {
-  return topk_k(dims, density, text_blocks, dense_extra_blocks, topk_override, k_out, nullptr);
+  return topk_k(dims, density, text_blocks, dense_extra_blocks, topk_override, k_out);
+}
+
+int32_t dbsp_select_nnz_bound_list(const dbsp_dims* dims, int32_t mode, double density_or_mass,
+                                   const int32_t* forced_blocks, int32_t n_forced,
+                                   int32_t topk_override, int64_t* nnz_bound_out) {
+  if (!shape_ok(dims) || !nnz_bound_out) return DBSP_ERR_INVALID_ARG;
+  ForcedSet fs;
+  const int32_t st = forced_from_list(dims->lk / DBSP_BLOCK, forced_blocks, n_forced, &fs);
+  if (st != DBSP_OK) return st;
+  return nnz_bound_f(dims, mode, density_or_mass, fs, topk_override, nnz_bound_out);
 }
 
 int32_t dbsp_select_nnz_bound(const dbsp_dims* dims, int32_t mode, double density_or_mass,
@@ -213,12 +283,13 @@ int32_t dbsp_select_workspace_bytes(const dbsp_dims* dims, int32_t mode, uint64_
   return DBSP_OK;
 }
 
-int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
-                           dbsp_range text_blocks, dbsp_range dense_extra_blocks, int32_t mode,
-                           double density_or_mass, int32_t topk_override, float score_scale,
-                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                           float* scores_out, void* workspace, uint64_t workspace_bytes,
-                           void* stream) {
+static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims* dims,
+                                  const ForcedSet* fs_in, dbsp_range text_blocks,
+                                  dbsp_range dense_extra_blocks, int32_t mode,
+                                  double density_or_mass, int32_t topk_override, float score_scale,
+                                  int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                  float* scores_out, void* workspace, uint64_t workspace_bytes,
+                                  void* stream) {
   if (!shape_ok(dims) || !q || !k || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
   if (mode != DBSP_TOPK && mode != DBSP_MASS) return DBSP_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k)) return DBSP_ERR_INVALID_ARG;
@@ -227,9 +298,15 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
   const int32_t nkb = dims->lk / DBSP_BLOCK;
   const int32_t nqb = dims->lq / DBSP_BLOCK;
   if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  ForcedSet fs;
+  if (fs_in) {
+    fs = *fs_in;
+  } else {
+    const int32_t st = forced_from_ranges(nkb, text_blocks, dense_extra_blocks, &fs);
+    if (st != DBSP_OK) return st;
+  }
   int64_t bound;
-  int32_t st = nnz_bound(dims, mode, density_or_mass, text_blocks, dense_extra_blocks,
-                         topk_override, &bound);
+  int32_t st = nnz_bound_f(dims, mode, density_or_mass, fs, topk_override, &bound);
   if (st != DBSP_OK) return st;
   if (bound > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
   if (col_capacity < bound) return DBSP_ERR_CAPACITY;
@@ -252,10 +329,7 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
   a.nqb = nqb;
   a.nkb = nkb;
   a.scale = score_scale > 0.f ? score_scale : (float)(1.0 / sqrt((double)dims->head_dim));
-  a.t0 = text_blocks.begin;
-  a.t1 = text_blocks.end;
-  a.e0 = dense_extra_blocks.begin;
-  a.e1 = dense_extra_blocks.end;
+  apply_forced(fs, &a);
   a.mode = mode;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
@@ -264,10 +338,10 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
   a.lds_stride = score_lds_stride(nkb);
   a.n_rows = bh * nqb;
   if (mode == DBSP_TOPK) {
-    int32_t kk, f;
-    topk_k(dims, density_or_mass, text_blocks, dense_extra_blocks, topk_override, &kk, &f);
+    int32_t kk;
+    topk_k_f(dims, density_or_mass, fs, topk_override, &kk);
     a.kk = kk;
-    a.per_row = f + kk;
+    a.per_row = fs.count + kk;
   } else {
     a.keep_all = density_or_mass >= 1.0;
     a.theta = (uint64_t)ceil(density_or_mass * 4611686018427387904.0);  // tau * 2^62
@@ -277,6 +351,32 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
   }
   if (dbsp::launch_select(a, bh, dims->head_dim, bf16, s) != hipSuccess) return DBSP_ERR_HIP;
   return DBSP_OK;
+}
+
+int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
+                           dbsp_range text_blocks, dbsp_range dense_extra_blocks, int32_t mode,
+                           double density_or_mass, int32_t topk_override, float score_scale,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                           float* scores_out, void* workspace, uint64_t workspace_bytes,
+                           void* stream) {
+  return sparse_select_impl(q, k, dims, nullptr, text_blocks, dense_extra_blocks, mode,
+                            density_or_mass, topk_override, score_scale, row_ptr, col_idx,
+                            col_capacity, scores_out, workspace, workspace_bytes, stream);
+}
+
+int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* dims,
+                                const int32_t* forced_blocks, int32_t n_forced, int32_t mode,
+                                double density_or_mass, int32_t topk_override, float score_scale,
+                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                float* scores_out, void* workspace, uint64_t workspace_bytes,
+                                void* stream) {
+  if (!shape_ok(dims)) return DBSP_ERR_INVALID_ARG;
+  ForcedSet fs;
+  const int32_t st = forced_from_list(dims->lk / DBSP_BLOCK, forced_blocks, n_forced, &fs);
+  if (st != DBSP_OK) return st;
+  return sparse_select_impl(q, k, dims, &fs, dbsp_range{0, 0}, dbsp_range{0, 0}, mode,
+                            density_or_mass, topk_override, score_scale, row_ptr, col_idx,
+                            col_capacity, scores_out, workspace, workspace_bytes, stream);
 }
 
 int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
@@ -377,10 +477,9 @@ int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_rang
   dbsp::SelectArgs a{};
   a.nqb = dims->lq / DBSP_BLOCK;
   a.nkb = nkb;
-  a.t0 = text_blocks.begin;
-  a.t1 = text_blocks.end;
-  a.e0 = dense_extra_blocks.begin;
-  a.e1 = dense_extra_blocks.end;
+  ForcedSet fs;
+  forced_from_ranges(nkb, text_blocks, dense_extra_blocks, &fs);  // validated by nnz_bound
+  apply_forced(fs, &a);
   a.mode = DBSP_MASS;
   a.keep_all = mass >= 1.0;
   a.theta = (uint64_t)ceil(mass * 4611686018427387904.0);  // tau * 2^62

@@ -6,13 +6,18 @@
 
 namespace dbsp {
 
+// Largest forced set passed as a bitmask in the kernel arguments: one bit per key block.
+constexpr int kMaxForcedWords = 32;  // 2048 key blocks
+
 struct SelectArgs {
   const void* q;           // queries [BH, nqb * 128, D] (bf16 or fp32), pooled in the kernel
   const uint16_t* ksplit;  // pooled keys as bf16 hi | lo in MFMA tile order (workspace):
                            // [BH][ceil(nkb / 16)][D / 32][hi | lo][64 lanes][8]
   int nqb, nkb;
   float scale;         // score scale
-  int t0, t1, e0, e1;  // forced key-block ranges [t0, t1) and [e0, e1)
+  int t0, t1, e0, e1;  // forced key-block ranges [t0, t1) and [e0, e1) ...
+  int forced_by_words; // ... or, when set, the forced blocks are the set bits of forced_words
+  uint64_t forced_words[kMaxForcedWords];
   int mode;            // 0 Top-K, 1 mass
   int kk;              // Top-K: candidates kept per row
   int per_row;         // Top-K: entries per row (forced + kk)

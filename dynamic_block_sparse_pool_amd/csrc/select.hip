@@ -56,7 +56,10 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float(u);
 }
 
+// Callers pass 0 <= c < nkb <= 2048, so the word index is in range; it is uniform across a
+// wave (c = 64 e + lane), so the word comes from the kernel arguments through a scalar load.
 __device__ __forceinline__ bool is_forced(int c, const SelectArgs& a) {
+  if (a.forced_by_words) return (a.forced_words[c >> 6] >> (c & 63)) & 1ull;
   return (c >= a.t0 && c < a.t1) || (c >= a.e0 && c < a.e1);
 }
 

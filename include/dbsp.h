@@ -152,6 +152,28 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
                            void* stream);
 
 /*
+ * dbsp_sparse_select with the forced set F given as an explicit list of key-block indices
+ * instead of two ranges (the pages' forced segments are contiguous; a list covers any other
+ * layout of conditioning blocks). forced_blocks is HOST memory holding n_forced distinct
+ * indices in [0, lk / 128), in any order; it is read before the call returns (the set travels
+ * to the kernels in their launch arguments, so nothing is copied to the device). Everything
+ * else is as dbsp_sparse_select with F = the listed blocks.
+ * Errors: DBSP_ERR_INVALID_ARG for a negative count, a NULL list with n_forced > 0, an index out
+ * of range or a duplicate; otherwise as dbsp_sparse_select.
+ */
+int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* dims,
+                                const int32_t* forced_blocks, int32_t n_forced, int32_t mode,
+                                double density_or_mass, int32_t topk_override, float score_scale,
+                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                float* scores_out, void* workspace, uint64_t workspace_bytes,
+                                void* stream);
+
+/* dbsp_select_nnz_bound for a forced list (host memory, as dbsp_sparse_select_list). */
+int32_t dbsp_select_nnz_bound_list(const dbsp_dims* dims, int32_t mode, double density_or_mass,
+                                   const int32_t* forced_blocks, int32_t n_forced,
+                                   int32_t topk_override, int64_t* nnz_bound_out);
+
+/*
  * Block-sparse attention, forward only ([SparSTAR] FastFlex bullet; [CalibAtt] key design 4).
  *
  * For each CSR row r = (b, h, i) and each query t of block i:

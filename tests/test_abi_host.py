@@ -242,3 +242,34 @@ def test_vote_calls_reject_bad_arguments(lib):
     assert sel(ws=ctypes.c_void_p((1 << 20) + 16)) == E.DBSP_ERR_WORKSPACE
     ws = ctypes.c_uint64()
     assert lib.dbsp_vote_workspace_bytes(ctypes.byref(good), ctypes.byref(ws)) == 0 and ws.value > 0
+
+
+def test_forced_list_validation(lib):
+    E = _abi
+    dims = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_BF16)   # 8 key blocks, 4 rows
+
+    def bound(lst, mode=E.DBSP_TOPK, param=0.5):
+        arr = (ctypes.c_int32 * max(len(lst), 1))(*lst) if lst else None
+        out = ctypes.c_int64()
+        st = lib.dbsp_select_nnz_bound_list(ctypes.byref(dims), mode, param, arr, len(lst), -1,
+                                            ctypes.byref(out))
+        return st, out.value
+
+    # scattered list {1, 6}: |C| = 6, K = ceil(0.5 * 6) = 3 -> 4 rows x 5
+    assert bound([6, 1]) == (0, 4 * 5)
+    assert bound([]) == (0, 4 * 4)            # no forced block: K = ceil(0.5 * 8)
+    assert bound([3], E.DBSP_MASS, 0.9) == (0, 4 * 8)
+    for bad in ([8], [-1], [2, 2], [0, 5, 0]):
+        assert bound(bad)[0] == E.DBSP_ERR_INVALID_ARG, bad
+    # the same checks guard the select call itself, before any workspace check
+    arr = (ctypes.c_int32 * 2)(3, 3)
+    assert lib.dbsp_sparse_select_list(FAKE, FAKE, ctypes.byref(dims), arr, 2, E.DBSP_TOPK, 0.5,
+                                       -1, 0.0, FAKE, FAKE, 1 << 40, None, None, 0,
+                                       None) == E.DBSP_ERR_INVALID_ARG
+    assert lib.dbsp_sparse_select_list(FAKE, FAKE, ctypes.byref(dims), None, 1, E.DBSP_TOPK, 0.5,
+                                       -1, 0.0, FAKE, FAKE, 1 << 40, None, None, 0,
+                                       None) == E.DBSP_ERR_INVALID_ARG
+    ok = (ctypes.c_int32 * 2)(1, 6)
+    assert lib.dbsp_sparse_select_list(FAKE, FAKE, ctypes.byref(dims), ok, 2, E.DBSP_TOPK, 0.5,
+                                       -1, 0.0, FAKE, FAKE, 1 << 40, None, None, 0,
+                                       None) == E.DBSP_ERR_WORKSPACE

@@ -243,3 +243,41 @@ def test_bf16_output_rounds_fp32_output():
     o16 = dbsp().sparse_attn_fwd(q, k, v, idx, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("mode", ["topk", "mass"])
+def test_forced_list(mode):
+    # an explicit, scattered forced list (across bitmask words, unsorted) instead of ranges:
+    # masks bit-exact against the oracle selecting with that forced set from the GPU's scores
+    m = dbsp()
+    w = small_variants()["final_small"].with_(lk=(4 + 65 + 65) * BLOCK)
+    nkb = w.n_k_blocks
+    forced_list = [130, 0, 64, 63, 7, 101]
+    say(f"case forced list {forced_list} mode={mode} nkb={nkb}")
+    q, k, _ = make_qkv(w, device="cuda", seed=21)
+    kw = dict(density=0.2) if mode == "topk" else dict(mass=0.8)
+    idx = m.sparse_select(q, k, density=kw.get("density"), mass=kw.get("mass"),
+                          return_scores=True, forced_blocks=forced_list)
+    torch.cuda.synchronize()
+    forced = np.zeros(nkb, dtype=bool)
+    forced[forced_list] = True
+    scores = P.host(idx.scores)
+    if mode == "topk":
+        kk = oracle.topk_budget(0.2, int((~forced).sum()))
+        kept_ora = oracle.select_topk(scores, forced, kk)
+    else:
+        kept_ora = oracle.select_mass(scores, forced, 0.8)
+    rp = idx.row_ptr.cpu().numpy().astype(np.int64)
+    ci = idx.col_idx.cpu().numpy().astype(np.int64)
+    kept_gpu = P.csr_to_kept(rp, ci, nkb)
+    np.testing.assert_array_equal(kept_gpu, kept_ora)
+    assert kept_gpu[:, forced_list].all()
+    # the list equal to a range gives the range's result bit for bit
+    idx_r = m.sparse_select(q, k, (0, 4), density=kw.get("density"), mass=kw.get("mass"))
+    idx_l = m.sparse_select(q, k, density=kw.get("density"), mass=kw.get("mass"),
+                            forced_blocks=[3, 2, 1, 0])
+    torch.cuda.synchronize()
+    n = idx_r.nnz()
+    assert n == idx_l.nnz()
+    assert torch.equal(idx_r.row_ptr, idx_l.row_ptr)
+    assert torch.equal(idx_r.col_idx[:n], idx_l.col_idx[:n])
