@@ -37,7 +37,8 @@ def attention_rows(q, k, v, row_ptr, col_idx, rows: Optional[Iterable[int]] = No
     q [B, H, Lq, d], k and v [B, H, Lk, d]. Returns (O [n, block, d], lse [n, block]) in float64
     for the n listed rows (all rows if rows is None)."""
     bsz, heads, lq, d = q.shape
-    nqb = lq // block
+    lk = k.shape[-2]
+    nqb = -(-lq // block)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if rows is None:
@@ -51,11 +52,14 @@ def attention_rows(q, k, v, row_ptr, col_idx, rows: Optional[Iterable[int]] = No
         cols = np.asarray(col_idx[int(row_ptr[r]):int(row_ptr[r + 1])], dtype=np.int64)
         if cols.size == 0:
             continue
+        # tokens of the kept blocks; a partial last key block contributes the tokens it holds
         tok = (cols[:, None] * block + np.arange(block)[None, :]).reshape(-1)
-        qi = np.asarray(q[b, h, i * block:(i + 1) * block], dtype=np.float64)
+        tok = tok[tok < lk]
+        q0, q1 = i * block, min((i + 1) * block, lq)
+        qi = np.asarray(q[b, h, q0:q1], dtype=np.float64)
         kt = np.asarray(k[b, h], dtype=np.float64)[tok]
         vt = np.asarray(v[b, h], dtype=np.float64)[tok]
-        out[n], lse[n] = _softmax_weighted((qi @ kt.T) * scale, vt)
+        out[n, :q1 - q0], lse[n, :q1 - q0] = _softmax_weighted((qi @ kt.T) * scale, vt)
     return out, lse
 
 
@@ -70,7 +74,8 @@ def attention_masked(q, k, v, kept, scale: Optional[float] = None, block: int = 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     kept = np.asarray(kept, dtype=bool)
-    token_mask = np.repeat(np.repeat(kept, block, axis=-2), block, axis=-1)    # [B,H,Lq,Lk]
+    lq, lk = q.shape[-2], k.shape[-2]
+    token_mask = np.repeat(np.repeat(kept, block, axis=-2), block, axis=-1)[..., :lq, :lk]
     logits = np.where(token_mask, (q @ np.swapaxes(k, -1, -2)) * scale, -np.inf)
     m = logits.max(axis=-1, keepdims=True)
     empty = ~np.isfinite(m)

@@ -25,7 +25,7 @@ def block_energy_rows(q, k, rows: Iterable[int], scale: Optional[float] = None,
     q [B, H, Lq, d], k [B, H, Lk, d] -> E [n, nKB]."""
     bsz, heads, lq, d = q.shape
     lk = k.shape[-2]
-    nqb, nkb = lq // block, lk // block
+    nqb, nkb = -(-lq // block), -(-lk // block)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = list(rows)
@@ -33,12 +33,15 @@ def block_energy_rows(q, k, rows: Iterable[int], scale: Optional[float] = None,
     for n, r in enumerate(rows):
         bh, i = divmod(int(r), nqb)
         b, h = divmod(bh, heads)
-        qi = np.asarray(q[b, h, i * block:(i + 1) * block], dtype=np.float64)
+        # a partial last block holds fewer tokens; B is then the number it holds (reading)
+        qi = np.asarray(q[b, h, i * block:min((i + 1) * block, lq)], dtype=np.float64)
         kk = np.asarray(k[b, h], dtype=np.float64)
         logits = (qi @ kk.T) * scale
         e = np.exp(logits - logits.max(axis=1, keepdims=True))
-        p = e / e.sum(axis=1, keepdims=True)                     # [block, Lk]
-        out[n] = p.reshape(block, nkb, block).sum(axis=(0, 2)) / block
+        p = e / e.sum(axis=1, keepdims=True)                     # [queries, Lk]
+        per_key = p.sum(axis=0)
+        for c in range(nkb):
+            out[n, c] = per_key[c * block:min((c + 1) * block, lk)].sum() / qi.shape[0]
     return out
 
 
@@ -51,7 +54,7 @@ def token_upper_bound(q, k, rows: Iterable[int], budgets: Iterable[int],
     the dense softmax. No mask keeping m_r tokens per query retains more, so a block mask's
     retained mass is at most this value."""
     bsz, heads, lq, d = q.shape
-    nqb = lq // block
+    nqb = -(-lq // block)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows, budgets = list(rows), list(budgets)
@@ -59,7 +62,7 @@ def token_upper_bound(q, k, rows: Iterable[int], budgets: Iterable[int],
     for n, (r, m) in enumerate(zip(rows, budgets)):
         bh, i = divmod(int(r), nqb)
         b, h = divmod(bh, heads)
-        qi = np.asarray(q[b, h, i * block:(i + 1) * block], dtype=np.float64)
+        qi = np.asarray(q[b, h, i * block:min((i + 1) * block, lq)], dtype=np.float64)
         kk = np.asarray(k[b, h], dtype=np.float64)
         logits = (qi @ kk.T) * scale
         e = np.exp(logits - logits.max(axis=1, keepdims=True))

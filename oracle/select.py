@@ -32,22 +32,33 @@ MASS_BITS = 62       # fixed-point scale of the exact mass comparison (reading a
 
 
 def n_blocks(length: int, block: int = BLOCK) -> int:
-    """[SparSTAR] method overview, block partition: L tokens form L / 128 blocks; token t of a
-    sequence belongs to block t // 128. Lengths that are not a whole number of blocks are
-    rejected (the pages only describe whole blocks)."""
-    if length <= 0 or length % block:
-        raise ValueError(f"length {length} is not a positive multiple of the block size {block}")
-    return length // block
+    """[SparSTAR] method overview, block partition: token t of a sequence belongs to block
+    t // 128. Reading for lengths that are not a whole number of blocks (the pages only show
+    whole blocks): the last block is partial and holds the remaining tokens, so there are
+    ceil(L / 128) blocks."""
+    if length <= 0:
+        raise ValueError(f"length {length} is not positive")
+    return -(-length // block)
+
+
+def block_tokens(i: int, length: int, block: int = BLOCK) -> range:
+    """Token positions of block i (the last one may hold fewer than `block`)."""
+    return range(i * block, min((i + 1) * block, length))
 
 
 def pool(x, block: int = BLOCK) -> np.ndarray:
     """[SparSTAR] method overview, block partition bullet: the vectors inside each block are
-    averaged. x is [..., L, d]; the result is [..., L / block, d] in float64. Pooling runs
-    separately for every (batch, head) slice, never across heads ([SparSTAR] per-head bullet)."""
+    averaged. x is [..., L, d]; the result is [..., ceil(L / block), d] in float64; a partial last
+    block averages the tokens it holds. Pooling runs separately for every (batch, head) slice,
+    never across heads ([SparSTAR] per-head bullet)."""
     x = np.asarray(x, dtype=np.float64)
     length, d = x.shape[-2], x.shape[-1]
     nb = n_blocks(length, block)
-    return x.reshape(x.shape[:-2] + (nb, block, d)).mean(axis=-2)
+    out = np.empty(x.shape[:-2] + (nb, d), dtype=np.float64)
+    for i in range(nb):
+        t = block_tokens(i, length, block)
+        out[..., i, :] = x[..., t.start:t.stop, :].mean(axis=-2)
+    return out
 
 
 def block_scores(qbar, kbar, scale: Optional[float] = None) -> np.ndarray:

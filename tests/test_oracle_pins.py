@@ -26,12 +26,60 @@ def _load(name):
 
 # ---------------------------------------------------------------- partition and pooling
 
-def test_partition_whole_blocks_only():
+def test_partition_counts():
     assert oracle.n_blocks(1024) == 8
     assert oracle.n_blocks(144896) == 1132
-    for bad in (0, 127, 1000, -128):
+    # a partial last block holds the remaining tokens (the DiT's 75,600 video tokens: 590 full
+    # blocks and one of 80)
+    assert oracle.n_blocks(75600) == 591 and oracle.n_blocks(127) == 1 and oracle.n_blocks(129) == 2
+    assert list(oracle.select.block_tokens(590, 75600)) == list(range(75520, 75600))
+    for bad in (0, -128):
         with pytest.raises(ValueError):
             oracle.n_blocks(bad)
+
+
+def test_pool_partial_block_closed_form():
+    # x[t] = t: a full block averages to 128 i + 63.5; the partial last block of L = 300 tokens
+    # (tokens 256 .. 299) averages to 277.5
+    L = 300
+    x = np.arange(L, dtype=np.float64)[:, None] * np.ones((1, 2))
+    np.testing.assert_array_equal(oracle.pool(x)[:, 0], [63.5, 191.5, 277.5])
+
+
+def test_partial_blocks_match_sdpa_and_sum_to_one():
+    # lengths that are not block multiples: the masked and gathered attention agree with torch's
+    # float64 SDPA over the valid tokens, and token-level energies still sum to 1 per row
+    rng = np.random.default_rng(41)
+    lq, lk, d = 2 * BLOCK + 37, 3 * BLOCK + 5, 8
+    q = rng.standard_normal((1, 2, lq, d))
+    k = rng.standard_normal((1, 2, lk, d))
+    v = rng.standard_normal((1, 2, lk, d))
+    nqb, nkb = oracle.n_blocks(lq), oracle.n_blocks(lk)
+    kept = rng.random((1, 2, nqb, nkb)) < 0.6
+    kept[..., nkb - 1] = True                       # the partial key block is always used
+    row_ptr, col_idx = oracle.to_csr(kept.reshape(-1, nkb))
+    o1, l1 = oracle.attention_rows(q, k, v, row_ptr, col_idx)
+    o1 = o1.reshape(1, 2, nqb * BLOCK, d)[:, :, :lq]
+    l1 = l1.reshape(1, 2, nqb * BLOCK)[:, :, :lq]
+    o2, l2 = oracle.attention_masked(q, k, v, kept)
+    mask = torch.from_numpy(np.repeat(np.repeat(kept, BLOCK, axis=-2), BLOCK, axis=-1)[..., :lq, :lk])
+    o3 = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask).numpy()
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o1, o3, rtol=1e-10, atol=1e-12)
+    e = oracle.block_energy_rows(q, k, rows=range(2 * nqb))
+    np.testing.assert_allclose(e.sum(axis=1), 1.0, atol=1e-12)
+    # energies against SDPA over block indicators, with the partial query block's own count
+    ind = np.zeros((lk, nkb))
+    ind[np.arange(lk), np.arange(lk) // BLOCK] = 1.0
+    o_ind = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k),
+        torch.from_numpy(np.broadcast_to(ind, (1, 2, lk, nkb)).copy())).numpy()
+    for r in range(2 * nqb):
+        h, i = divmod(r, nqb)
+        t0, t1 = i * BLOCK, min((i + 1) * BLOCK, lq)
+        np.testing.assert_allclose(e[r], o_ind[0, h, t0:t1].mean(axis=0), rtol=1e-12, atol=1e-15)
 
 
 def test_pool_closed_form():
