@@ -47,6 +47,11 @@ class BlockIndex:
         return int(self.row_ptr[-1].item())
 
 
+def _nblocks(length: int) -> int:
+    """Blocks of a sequence: a length that is not a multiple of 128 ends in a partial block."""
+    return -(-int(length) // DBSP_BLOCK)
+
+
 def version() -> int:
     return int(_abi.load().dbsp_version())
 
@@ -144,8 +149,8 @@ class SelectPlan:
         self.topk_override = int(topk_override)
         self.score_scale = float(score_scale)
         self.device = q.device
-        rows = self.dims.batch * self.dims.heads * (self.dims.lq // DBSP_BLOCK)
-        nkb = self.dims.lk // DBSP_BLOCK
+        rows = self.dims.batch * self.dims.heads * (_nblocks(self.dims.lq))
+        nkb = _nblocks(self.dims.lk)
         if self.forced is None:
             self.capacity = select_nnz_bound(self.dims, self.mode, self.param, text_blocks,
                                              dense_extra_blocks, self.topk_override)
@@ -161,7 +166,7 @@ class SelectPlan:
         self.col_idx = torch.empty(max(self.capacity, 1), dtype=torch.int32, device=q.device)
         self.scores = (torch.empty((rows, nkb), dtype=torch.float32, device=q.device)
                        if return_scores else None)
-        self.index = BlockIndex(self.row_ptr, self.col_idx, self.dims.lq // DBSP_BLOCK, nkb,
+        self.index = BlockIndex(self.row_ptr, self.col_idx, _nblocks(self.dims.lq), nkb,
                                 self.scores)
 
     def run(self, q: torch.Tensor, k: torch.Tensor) -> BlockIndex:
@@ -212,7 +217,7 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
     dims = _dims(q, k)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    rows = dims.batch * dims.heads * (dims.lq // DBSP_BLOCK)
+    rows = dims.batch * dims.heads * (_nblocks(dims.lq))
     if index.row_ptr.numel() != rows + 1:
         raise ValueError("index was built for a different shape")
     if index.row_ptr.dtype != torch.int32 or index.col_idx.dtype != torch.int32:
@@ -240,8 +245,8 @@ def block_energy(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0,
     _check_device_tensor("q", q)
     _check_device_tensor("k", k)
     dims = _dims(q, k)
-    rows = dims.batch * dims.heads * (dims.lq // DBSP_BLOCK)
-    nkb = dims.lk // DBSP_BLOCK
+    rows = dims.batch * dims.heads * (_nblocks(dims.lq))
+    nkb = _nblocks(dims.lk)
     if out is None:
         out = torch.empty((rows, nkb), dtype=torch.float32, device=q.device)
     elif out.shape != (rows, nkb) or out.dtype != torch.float32 or not out.is_contiguous():
@@ -298,7 +303,7 @@ def select_energy(energy: torch.Tensor, mass: float, text_blocks=(0, 0),
                                 _ptr(col_idx), col_idx.numel(), _ptr(ws), ws.numel(),
                                 _stream(energy.device))
     _abi.check(st, "dbsp_select_energy")
-    return BlockIndex(row_ptr, col_idx, dims.lq // DBSP_BLOCK, nkb, None)
+    return BlockIndex(row_ptr, col_idx, _nblocks(dims.lq), nkb, None)
 
 
 class MaskVote:

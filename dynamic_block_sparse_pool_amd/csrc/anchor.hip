@@ -136,6 +136,8 @@ hipError_t launch_anchor(const AnchorArgs& a, int head_dim, bool bf16, hipStream
   at.col_capacity = rows_a * a.nkb;
   at.nqb = (int)(g.la_pad / kBlock);
   at.nkb = a.nkb;
+  at.lq = g.la_pad;
+  at.lk = a.lk;
   at.rows = rows_a;
   at.scale_log2 = a.scale_log2;
   at.o = a.oa;

@@ -17,11 +17,14 @@ constexpr int32_t kMaxBf16KeyBlocks = 65535;
 bool shape_ok(const dbsp_dims* d) {
   if (!d) return false;
   if (d->batch <= 0 || d->heads <= 0 || d->lq <= 0 || d->lk <= 0) return false;
-  if (d->lq % DBSP_BLOCK || d->lk % DBSP_BLOCK) return false;
   if (d->dtype != DBSP_F32 && d->dtype != DBSP_BF16) return false;
   if (d->head_dim <= 0) return false;
   return true;
 }
+
+// Blocks per sequence: a length that is not a multiple of 128 ends in a partial block.
+int32_t nqb_of(const dbsp_dims* d) { return (d->lq + DBSP_BLOCK - 1) / DBSP_BLOCK; }
+int32_t nkb_of(const dbsp_dims* d) { return (d->lk + DBSP_BLOCK - 1) / DBSP_BLOCK; }
 
 bool dtype_supported(const dbsp_dims* d) {
   if (d->dtype == DBSP_BF16) return d->head_dim == 128 || d->head_dim == 64;
@@ -34,7 +37,7 @@ bool attn_supported(const dbsp_dims* d) {
 }
 
 int64_t rows_of(const dbsp_dims* d) {
-  return (int64_t)d->batch * d->heads * (d->lq / DBSP_BLOCK);
+  return (int64_t)d->batch * d->heads * nqb_of(d);
 }
 
 // Validates the two forced ranges against nkb; returns the forced count or -1.
@@ -87,7 +90,7 @@ int32_t forced_from_list(int32_t nkb, const int32_t* list, int32_t n, ForcedSet*
 int32_t topk_k_f(const dbsp_dims* d, double density, const ForcedSet& fs, int32_t override_k,
                  int32_t* k_out) {
   if (!shape_ok(d) || !k_out) return DBSP_ERR_INVALID_ARG;
-  const int32_t nkb = d->lk / DBSP_BLOCK;
+  const int32_t nkb = nkb_of(d);
   const int32_t ncand = nkb - fs.count;
   int64_t k;
   if (override_k >= 0) {
@@ -106,7 +109,7 @@ int32_t topk_k(const dbsp_dims* d, double density, dbsp_range t, dbsp_range e, i
                int32_t* k_out) {
   if (!shape_ok(d) || !k_out) return DBSP_ERR_INVALID_ARG;
   ForcedSet fs;
-  const int32_t st = forced_from_ranges(d->lk / DBSP_BLOCK, t, e, &fs);
+  const int32_t st = forced_from_ranges(nkb_of(d), t, e, &fs);
   if (st != DBSP_OK) return st;
   return topk_k_f(d, density, fs, override_k, k_out);
 }
@@ -114,7 +117,7 @@ int32_t topk_k(const dbsp_dims* d, double density, dbsp_range t, dbsp_range e, i
 int32_t nnz_bound_f(const dbsp_dims* d, int32_t mode, double param, const ForcedSet& fs,
                     int32_t override_k, int64_t* out) {
   if (!shape_ok(d) || !out) return DBSP_ERR_INVALID_ARG;
-  const int32_t nkb = d->lk / DBSP_BLOCK;
+  const int32_t nkb = nkb_of(d);
   if (mode == DBSP_TOPK) {
     int32_t k;
     const int32_t st = topk_k_f(d, param, fs, override_k, &k);
@@ -134,7 +137,7 @@ int32_t nnz_bound(const dbsp_dims* d, int32_t mode, double param, dbsp_range t, 
                   int32_t override_k, int64_t* out) {
   if (!shape_ok(d) || !out) return DBSP_ERR_INVALID_ARG;
   ForcedSet fs;
-  const int32_t st = forced_from_ranges(d->lk / DBSP_BLOCK, t, e, &fs);
+  const int32_t st = forced_from_ranges(nkb_of(d), t, e, &fs);
   if (st != DBSP_OK) return st;
   return nnz_bound_f(d, mode, param, fs, override_k, out);
 }
@@ -165,7 +168,7 @@ struct WorkspaceLayout {
 WorkspaceLayout layout_of(const dbsp_dims* d, int32_t mode) {
   WorkspaceLayout w{};
   const uint64_t bh = (uint64_t)d->batch * d->heads;
-  const uint64_t nqb = d->lq / DBSP_BLOCK, nkb = d->lk / DBSP_BLOCK;
+  const uint64_t nqb = nqb_of(d), nkb = nkb_of(d);
   uint64_t off = 0;
   // pooled keys, each stored as bf16 hi and lo halves (2 x head_dim x 2 bytes); the pooled
   // queries never leave the selection kernel
@@ -206,7 +209,7 @@ int32_t anchor_layout(const dbsp_dims* d, int32_t frames, int32_t rows, int32_t 
   const uint64_t bh = (uint64_t)d->batch * d->heads;
   const uint64_t in_elt = d->dtype == DBSP_BF16 ? 2 : 4, out_elt = o_dtype == DBSP_BF16 ? 2 : 4;
   const uint64_t rows_a = bh * (uint64_t)(l.g.la_pad / DBSP_BLOCK);
-  const uint64_t nkb = d->lk / DBSP_BLOCK;
+  const uint64_t nkb = nkb_of(d);
   if (rows_a * nkb > (uint64_t)INT32_MAX) return DBSP_ERR_UNSUPPORTED;
   uint64_t off = 0;
   l.qa = off;
@@ -227,7 +230,7 @@ int32_t anchor_layout(const dbsp_dims* d, int32_t frames, int32_t rows, int32_t 
 // dbsp_select_energy: per-row counts and kept bitmasks only.
 WorkspaceLayout energy_select_layout(const dbsp_dims* d) {
   WorkspaceLayout w{};
-  const uint64_t rows = (uint64_t)rows_of(d), nkb = d->lk / DBSP_BLOCK;
+  const uint64_t rows = (uint64_t)rows_of(d), nkb = nkb_of(d);
   w.counts = 0;
   w.masks = align256(rows * sizeof(int32_t));
   w.total = align256(w.masks + rows * ((nkb + 63) / 64) * sizeof(uint64_t));
@@ -264,7 +267,7 @@ int32_t dbsp_select_nnz_bound_list(const dbsp_dims* dims, int32_t mode, double d
                                    int32_t topk_override, int64_t* nnz_bound_out) {
   if (!shape_ok(dims) || !nnz_bound_out) return DBSP_ERR_INVALID_ARG;
   ForcedSet fs;
-  const int32_t st = forced_from_list(dims->lk / DBSP_BLOCK, forced_blocks, n_forced, &fs);
+  const int32_t st = forced_from_list(nkb_of(dims), forced_blocks, n_forced, &fs);
   if (st != DBSP_OK) return st;
   return nnz_bound_f(dims, mode, density_or_mass, fs, topk_override, nnz_bound_out);
 }
@@ -295,8 +298,8 @@ static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims*
   if (!aligned16(q) || !aligned16(k)) return DBSP_ERR_INVALID_ARG;
   if (!(isfinite(score_scale))) return DBSP_ERR_INVALID_ARG;
   if (!dtype_supported(dims)) return DBSP_ERR_UNSUPPORTED;
-  const int32_t nkb = dims->lk / DBSP_BLOCK;
-  const int32_t nqb = dims->lq / DBSP_BLOCK;
+  const int32_t nkb = nkb_of(dims);
+  const int32_t nqb = nqb_of(dims);
   if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
   ForcedSet fs;
   if (fs_in) {
@@ -319,8 +322,7 @@ static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims*
   const int64_t bh = (int64_t)dims->batch * dims->heads;
   uint16_t* ksplit = reinterpret_cast<uint16_t*>(ws + wl.kbar);
   const bool bf16 = dims->dtype == DBSP_BF16;
-  if (dbsp::launch_pool(nullptr, k, nullptr, ksplit, 0, bh * nkb, nkb, dims->head_dim, bf16, s) !=
-      hipSuccess)
+  if (dbsp::launch_pool(k, ksplit, bh, nkb, dims->lk, dims->head_dim, bf16, s) != hipSuccess)
     return DBSP_ERR_HIP;
 
   dbsp::SelectArgs a{};
@@ -328,6 +330,8 @@ static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims*
   a.ksplit = ksplit;
   a.nqb = nqb;
   a.nkb = nkb;
+  a.lq = dims->lq;
+  a.lk = dims->lk;
   a.scale = score_scale > 0.f ? score_scale : (float)(1.0 / sqrt((double)dims->head_dim));
   apply_forced(fs, &a);
   a.mode = mode;
@@ -372,7 +376,7 @@ int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* d
                                 void* stream) {
   if (!shape_ok(dims)) return DBSP_ERR_INVALID_ARG;
   ForcedSet fs;
-  const int32_t st = forced_from_list(dims->lk / DBSP_BLOCK, forced_blocks, n_forced, &fs);
+  const int32_t st = forced_from_list(nkb_of(dims), forced_blocks, n_forced, &fs);
   if (st != DBSP_OK) return st;
   return sparse_select_impl(q, k, dims, &fs, dbsp_range{0, 0}, dbsp_range{0, 0}, mode,
                             density_or_mass, topk_override, score_scale, row_ptr, col_idx,
@@ -390,7 +394,7 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
     return DBSP_ERR_INVALID_ARG;
   if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
   if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
-  if (dims->dtype == DBSP_BF16 && dims->lk / DBSP_BLOCK > kMaxBf16KeyBlocks)
+  if (dims->dtype == DBSP_BF16 && nkb_of(dims) > kMaxBf16KeyBlocks)
     return DBSP_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.f ? softmax_scale
                                           : (float)(1.0 / sqrt((double)dims->head_dim));
@@ -402,8 +406,10 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
   a.col_idx = col_idx;
   a.col_capacity = col_capacity;
   a.heads = dims->heads;
-  a.nqb = dims->lq / DBSP_BLOCK;
-  a.nkb = dims->lk / DBSP_BLOCK;
+  a.nqb = nqb_of(dims);
+  a.nkb = nkb_of(dims);
+  a.lq = dims->lq;
+  a.lk = dims->lk;
   a.rows = rows_of(dims);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o = o;
@@ -422,14 +428,16 @@ int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, f
     return DBSP_ERR_INVALID_ARG;
   if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
   if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
-  if (dims->lk / DBSP_BLOCK > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  if (nkb_of(dims) > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.f ? softmax_scale
                                           : (float)(1.0 / sqrt((double)dims->head_dim));
   dbsp::EnergyArgs a{};
   a.q = q;
   a.k = k;
-  a.nqb = dims->lq / DBSP_BLOCK;
-  a.nkb = dims->lk / DBSP_BLOCK;
+  a.nqb = nqb_of(dims);
+  a.nkb = nkb_of(dims);
+  a.lq = dims->lq;
+  a.lk = dims->lk;
   a.rows = rows_of(dims);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.energy = energy;
@@ -445,7 +453,7 @@ int32_t dbsp_retained_mass(const float* energy, const dbsp_dims* dims, const int
                            void* stream) {
   if (!shape_ok(dims) || !energy || !row_ptr || !mass) return DBSP_ERR_INVALID_ARG;
   if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
-  if (dbsp::launch_retained_mass(energy, row_ptr, col_idx, col_capacity, dims->lk / DBSP_BLOCK,
+  if (dbsp::launch_retained_mass(energy, row_ptr, col_idx, col_capacity, nkb_of(dims),
                                  rows_of(dims), mass, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DBSP_ERR_HIP;
@@ -463,7 +471,7 @@ int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_rang
                            int32_t* col_idx, int64_t col_capacity, void* workspace,
                            uint64_t workspace_bytes, void* stream) {
   if (!shape_ok(dims) || !energy || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
-  const int32_t nkb = dims->lk / DBSP_BLOCK;
+  const int32_t nkb = nkb_of(dims);
   if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
   int64_t bound;
   const int32_t st = nnz_bound(dims, DBSP_MASS, mass, text_blocks, dense_extra_blocks, -1, &bound);
@@ -475,7 +483,7 @@ int32_t dbsp_select_energy(const float* energy, const dbsp_dims* dims, dbsp_rang
     return DBSP_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   dbsp::SelectArgs a{};
-  a.nqb = dims->lq / DBSP_BLOCK;
+  a.nqb = nqb_of(dims);
   a.nkb = nkb;
   ForcedSet fs;
   forced_from_ranges(nkb, text_blocks, dense_extra_blocks, &fs);  // validated by nnz_bound
@@ -499,7 +507,7 @@ int32_t dbsp_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx, int
                              const dbsp_dims* dims, int32_t* counts, void* stream) {
   if (!shape_ok(dims) || !row_ptr || !counts) return DBSP_ERR_INVALID_ARG;
   if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
-  if (dbsp::launch_vote_accumulate(row_ptr, col_idx, col_capacity, dims->lk / DBSP_BLOCK,
+  if (dbsp::launch_vote_accumulate(row_ptr, col_idx, col_capacity, nkb_of(dims),
                                    rows_of(dims), counts, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DBSP_ERR_HIP;
@@ -517,7 +525,7 @@ int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n
                          void* workspace, uint64_t workspace_bytes, void* stream) {
   if (!shape_ok(dims) || !counts || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
   if (n_inputs < 1 || !(rho >= 0.0 && rho <= 1.0)) return DBSP_ERR_INVALID_ARG;  // rejects NaN
-  const int32_t nkb = dims->lk / DBSP_BLOCK;
+  const int32_t nkb = nkb_of(dims);
   if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
   const int64_t bound = rows_of(dims) * (int64_t)nkb;
   if (bound > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
@@ -527,7 +535,7 @@ int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n
     return DBSP_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   dbsp::SelectArgs a{};
-  a.nqb = dims->lq / DBSP_BLOCK;
+  a.nqb = nqb_of(dims);
   a.nkb = nkb;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
@@ -567,7 +575,7 @@ int32_t dbsp_anchor_attn_fwd(const void* q, const void* k, const void* v, const 
   const int32_t st = anchor_layout(dims, frames, rows_per_frame, row_width, n_anchors, o_dtype, &l);
   if (st != DBSP_OK) return st;
   if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
-  if (dims->dtype == DBSP_BF16 && dims->lk / DBSP_BLOCK > kMaxBf16KeyBlocks)
+  if (dims->dtype == DBSP_BF16 && nkb_of(dims) > kMaxBf16KeyBlocks)
     return DBSP_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace & 255u))
     return DBSP_ERR_WORKSPACE;
@@ -584,7 +592,8 @@ int32_t dbsp_anchor_attn_fwd(const void* q, const void* k, const void* v, const 
   a.row_ptr = reinterpret_cast<int32_t*>(ws + l.row_ptr);
   a.col_idx = reinterpret_cast<int32_t*>(ws + l.col_idx);
   a.bh = (int64_t)dims->batch * dims->heads;
-  a.nkb = dims->lk / DBSP_BLOCK;
+  a.nkb = nkb_of(dims);
+  a.lk = dims->lk;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o = o;
   a.o_bf16 = o_dtype == DBSP_BF16;

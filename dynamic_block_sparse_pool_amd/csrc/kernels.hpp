@@ -14,6 +14,7 @@ struct SelectArgs {
   const uint16_t* ksplit;  // pooled keys as bf16 hi | lo in MFMA tile order (workspace):
                            // [BH][ceil(nkb / 16)][D / 32][hi | lo][64 lanes][8]
   int nqb, nkb;
+  int64_t lq, lk;      // tokens per (batch, head); the last block may be partial
   float scale;         // score scale
   int t0, t1, e0, e1;  // forced key-block ranges [t0, t1) and [e0, e1) ...
   int forced_by_words; // ... or, when set, the forced blocks are the set bits of forced_words
@@ -42,6 +43,7 @@ struct AttnArgs {
   const int32_t* col_idx;
   int64_t col_capacity;
   int heads, nqb, nkb;
+  int64_t lq, lk;    // tokens per (batch, head); the last block may be partial
   int64_t rows;
   float scale_log2;  // softmax_scale * log2(e)
   void* o;
@@ -53,6 +55,7 @@ struct EnergyArgs {
   const void* q;
   const void* k;
   int nqb, nkb;
+  int64_t lq, lk;    // tokens per (batch, head); the last block may be partial
   int64_t rows;
   float scale_log2;  // softmax_scale * log2(e)
   float* energy;     // [rows, nkb]
@@ -78,6 +81,7 @@ struct AnchorArgs {
   int32_t* col_idx;
   int64_t bh;
   int nkb;
+  int64_t lk;        // key tokens per (batch, head)
   float scale_log2;
   void* o;
   int o_bf16;
@@ -85,9 +89,9 @@ struct AnchorArgs {
   AnchorGeom geom;
 };
 
-hipError_t launch_pool(const void* q, const void* k, uint16_t* qsplit, uint16_t* ksplit,
-                       int64_t nq_blocks, int64_t nk_blocks, int nkb, int head_dim, bool bf16,
-                       hipStream_t stream);
+// Pooled keys of every (batch, head): bh heads of lk tokens each, nkb = ceil(lk / 128) blocks.
+hipError_t launch_pool(const void* k, uint16_t* ksplit, int64_t bh, int nkb, int64_t lk,
+                       int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, bool bf16,
                          hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream);

@@ -1,13 +1,13 @@
-// Block mean pooling of Q and K ([SparSTAR] "SparSTAR：为什么视频自回归的稀疏注意力不能跨尺度复用？",
-// method overview, block partition bullet: the vectors inside each 128-token block are averaged).
+// Block mean pooling of K ([SparSTAR] "SparSTAR：为什么视频自回归的稀疏注意力不能跨尺度复用？",
+// method overview, block partition bullet: the vectors inside each 128-token block are averaged;
+// a partial last block, when lk is not a multiple of 128, averages the tokens it holds).
 //
-// One launch pools every Q block and every K block. Workgroup g < nq_blocks reads Q block g,
-// the rest read K blocks; a block is 128 consecutive rows of head_dim elements, contiguous in
-// memory (32 KiB for bf16 x 128 or fp32 x 64). Each of the 256 threads owns one 16-byte column
-// chunk of 128 / (256 / chunks) rows, issues all of its loads before any arithmetic, sums in
-// fp32, and the partial column sums meet in LDS. Output per block: the fp32 mean m split as
-// hi = bf16(m) and lo = bf16(m - hi): queries as [hi(head_dim) | lo(head_dim)] bf16 per block,
-// keys in the tiled operand order of the scoring MFMAs (see ktile_offset). HBM-bound: every input byte is read exactly once.
+// One workgroup per key block of a (batch, head): up to 128 consecutive rows of head_dim
+// elements, contiguous in memory. Each of the 256 threads owns one 16-byte column chunk of
+// 128 / (256 / chunks) rows, issues all of its loads before any arithmetic (rows past the end of
+// a partial block are not read), sums in fp32, and the partial column sums meet in LDS. Output
+// per block: the fp32 mean m split as hi = bf16(m) and lo = bf16(m - hi), in the tiled operand
+// order of the scoring MFMAs (see ktile_offset). HBM-bound: every input byte is read once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,11 +26,9 @@ __device__ __forceinline__ int64_t ktile_offset(int64_t bh, int n, int ntiles, i
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ q,
-                                                          const T* __restrict__ k,
-                                                          uint16_t* __restrict__ qbar,
-                                                          uint16_t* __restrict__ kbar,
-                                                          int64_t nq_blocks, int nkb) {
+__global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ k,
+                                                          uint16_t* __restrict__ kbar, int nkb,
+                                                          int64_t lk) {
   constexpr int kVec = 16 / (int)sizeof(T);       // elements per 16-byte chunk
   constexpr int kChunks = D / kVec;               // chunks per row
   constexpr int kRowsPerPass = 256 / kChunks;     // rows covered by one pass of the workgroup
@@ -39,20 +37,24 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
 
   __shared__ float partial[kRowsPerPass][D + 1];
 
-  int64_t g = blockIdx.x;
-  const T* src;
-  const bool is_q = g < nq_blocks;
-  if (!is_q) g -= nq_blocks;
-  src = (is_q ? q : k) + g * (int64_t)kBlock * D;
+  const int64_t g = blockIdx.x;
+  const int64_t bh = g / nkb;
+  const int n = (int)(g - bh * nkb);
+  const int64_t first = (int64_t)n * kBlock;
+  const int valid = (int)(lk - first < kBlock ? lk - first : kBlock);  // 1 .. 128
+  const T* src = k + (bh * lk + first) * D;
   const int t = threadIdx.x;
   const int chunk = t % kChunks;
   const int row0 = t / kChunks;
 
   u32x4 raw[kPasses];
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p)
-    raw[p] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(src + (int64_t)(row0 + p * kRowsPerPass) * D) + chunk);
+  for (int p = 0; p < kPasses; ++p) {
+    const int row = row0 + p * kRowsPerPass;
+    raw[p] = row < valid ? __builtin_nontemporal_load(
+                               reinterpret_cast<const u32x4*>(src + (int64_t)row * D) + chunk)
+                         : u32x4{0u, 0u, 0u, 0u};
+  }
 
   float acc[kVec];
 #pragma unroll
@@ -77,38 +79,28 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < kRowsPerPass; ++r) s += partial[r][col];
-    const float m = s * (1.0f / kBlock);
+    const float m = valid == kBlock ? s * (1.0f / kBlock) : s / (float)valid;
     const uint32_t hi = f32_to_bf16_bits(m);
     const uint16_t lo = (uint16_t)f32_to_bf16_bits(m - __uint_as_float(hi << 16));
-    if (is_q) {
-      qbar[g * 2 * D + col] = (uint16_t)hi;
-      qbar[g * 2 * D + D + col] = lo;
-    } else {
-      const int64_t bh = g / nkb;
-      const int n = (int)(g - bh * nkb);
-      const int ntiles = (nkb + 15) >> 4;
-      kbar[ktile_offset<D>(bh, n, ntiles, col, 0)] = (uint16_t)hi;
-      kbar[ktile_offset<D>(bh, n, ntiles, col, 1)] = lo;
-    }
+    const int ntiles = (nkb + 15) >> 4;
+    kbar[ktile_offset<D>(bh, n, ntiles, col, 0)] = (uint16_t)hi;
+    kbar[ktile_offset<D>(bh, n, ntiles, col, 1)] = lo;
   }
 }
 
-hipError_t launch_pool(const void* q, const void* k, uint16_t* qbar, uint16_t* kbar,
-                       int64_t nq_blocks, int64_t nk_blocks, int nkb, int head_dim, bool bf16,
-                       hipStream_t stream) {
-  dim3 grid((unsigned)(nq_blocks + nk_blocks)), block(256);
+hipError_t launch_pool(const void* k, uint16_t* kbar, int64_t bh, int nkb, int64_t lk,
+                       int head_dim, bool bf16, hipStream_t stream) {
+  dim3 grid((unsigned)(bh * nkb)), block(256);
   if (bf16 && head_dim == 128)
-    pool_blocks_kernel<uint16_t, 128><<<grid, block, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, nq_blocks, nkb);
+    pool_blocks_kernel<uint16_t, 128><<<grid, block, 0, stream>>>((const uint16_t*)k, kbar, nkb,
+                                                                   lk);
   else if (bf16 && head_dim == 64)
-    pool_blocks_kernel<uint16_t, 64><<<grid, block, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, nq_blocks, nkb);
+    pool_blocks_kernel<uint16_t, 64><<<grid, block, 0, stream>>>((const uint16_t*)k, kbar, nkb,
+                                                                  lk);
   else if (!bf16 && head_dim == 64)
-    pool_blocks_kernel<float, 64><<<grid, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                               qbar, kbar, nq_blocks, nkb);
+    pool_blocks_kernel<float, 64><<<grid, block, 0, stream>>>((const float*)k, kbar, nkb, lk);
   else if (!bf16 && head_dim == 128)
-    pool_blocks_kernel<float, 128><<<grid, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                                qbar, kbar, nq_blocks, nkb);
+    pool_blocks_kernel<float, 128><<<grid, block, 0, stream>>>((const float*)k, kbar, nkb, lk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

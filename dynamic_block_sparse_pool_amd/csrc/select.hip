@@ -95,10 +95,16 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
   const int rr0 = 2 * wave;
   const bool live0 = row0 + rr0 < a.nqb, live1 = row0 + rr0 + 1 < a.nqb;
   if (!live0) return;
-  const T* src0 = static_cast<const T*>(a.q) + ((int64_t)bh * a.nqb + row0 + rr0) * kBlock * D +
+  const int64_t first0 = (int64_t)(row0 + rr0) * kBlock;  // first token of block rr0
+  const T* src0 = static_cast<const T*>(a.q) + ((int64_t)bh * a.lq + first0) * D +
                   (int64_t)r0 * D + chunk * kVec;
   // the second block is only read when it exists; otherwise the first is read twice
   const T* src1 = live1 ? src0 + (int64_t)kBlock * D : src0;
+  // tokens held by each block (a partial last block holds fewer than 128; rows past it are
+  // not read)
+  const int valid0 = (int)(a.lq - first0 < kBlock ? a.lq - first0 : kBlock);
+  const int64_t first1 = first0 + kBlock;
+  const int valid1 = live1 ? (int)(a.lq - first1 < kBlock ? a.lq - first1 : kBlock) : valid0;
   float acc0[kVec], acc1[kVec];
 #pragma unroll
   for (int e = 0; e < kVec; ++e) acc0[e] = acc1[e] = 0.f;
@@ -119,9 +125,12 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
     u32x4 raw0[kBatch], raw1[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
+      const int row = (b + i) * kRowsPerLoad + r0;
       const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
-      raw0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off));
-      raw1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off));
+      raw0[i] = row < valid0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off))
+                             : u32x4{0u, 0u, 0u, 0u};
+      raw1[i] = row < valid1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off))
+                             : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
@@ -141,10 +150,11 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
     for (int j = 0; j < 2; ++j) {
       if (j == 1 && !live1) break;
       const float* acc = j == 0 ? acc0 : acc1;
+      const int valid = j == 0 ? valid0 : valid1;
       uint16_t* dst = qlds + (rr0 + j) * 2 * D + chunk * kVec;
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
-        const float m = acc[e] * (1.0f / kBlock);
+        const float m = valid == kBlock ? acc[e] * (1.0f / kBlock) : acc[e] / (float)valid;
         const uint32_t hi = f32_to_bf16_bits(m);
         dst[e] = (uint16_t)hi;
         dst[D + e] = (uint16_t)f32_to_bf16_bits(m - __uint_as_float(hi << 16));

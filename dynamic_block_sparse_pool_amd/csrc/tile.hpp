@@ -76,6 +76,47 @@ __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t src, int tile_of
                                              0);
 }
 
+// S^T tiles of one key block: sacc[jt] holds keys 32 jt .. 32 jt + 31 (rows) x the wave's 32
+// queries; qf is the B operand (queries as columns) held in registers.
+__device__ __forceinline__ void qk_block(const uint16_t* k_tile, const bf16x8 (&qf)[8], int l32,
+                                         int h, f32x16 (&sacc)[4]) {
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
+    const int kr = 32 * jt + l32;
+    const uint16_t* krow = k_tile + kr * 128;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + k_swz(kr, 2 * s + h) * 8);
+      sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[jt], 0, 0, 0);
+    }
+  }
+}
+
+// Key row (within its 128-key tile) of accumulator register r of sacc[jt] in lane half h: the
+// 32x32 MFMA result layout puts row 8 (r / 4) + 4 h + r % 4 of the 32-row tile jt in register r.
+__device__ __forceinline__ int sacc_key(int jt, int r, int h) {
+  return 32 * jt + 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+// Plain (not DMA) copy of a partial tile: rows [0, valid) of `src` (128 bf16 per row) into the
+// swizzled LDS layout, rows [valid, 128) zero-filled. All 256 threads of the workgroup take
+// part; the caller synchronises before and after.
+template <bool kIsV>
+__device__ __forceinline__ void tile_load_partial(const uint16_t* src, int valid, uint16_t* lds,
+                                                  int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = tid + 256 * i;  // 16-byte chunk of the tile
+    const int row = q >> 4, lc = q & 15;
+    const u32x4 v = row < valid ? *reinterpret_cast<const u32x4*>(src + row * 128 + lc * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
+    const int pc = kIsV ? v_swz(row, lc) : k_swz(row, lc);
+    *reinterpret_cast<u32x4*>(lds + row * 128 + pc * 8) = v;
+  }
+}
+
 __device__ __forceinline__ int64_t clip64(int64_t x, int64_t lo, int64_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }

@@ -32,8 +32,12 @@
  *
  * Conventions shared by every call
  *   Layout     Q is [batch, heads, lq, head_dim]; K and V are [batch, heads, lk, head_dim];
- *              all contiguous row-major and 16-byte aligned. lq and lk are multiples of 128.
- *              Block i of a sequence is tokens [128 i, 128 i + 128).
+ *              all contiguous row-major and 16-byte aligned. lq, lk >= 1.
+ *              Block i of a sequence is tokens [128 i, min(128 i + 128, L)): a length that is
+ *              not a multiple of 128 ends in a partial block, which pools to the mean of the
+ *              tokens it holds and contributes only those tokens to attention and energies
+ *              (queries past the end are not written). There are ceil(L / 128) blocks; every
+ *              "lk / 128" below means that count.
  *   Rows       CSR row r = (b * heads + h) * (lq / 128) + i for batch b, head h, query block i.
  *              col_idx of a row lists key-block indices in strictly ascending order.
  *   Types      dtype DBSP_BF16 (head_dim 128) or DBSP_F32 (head_dim 64 or 128).
@@ -201,7 +205,8 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
  * Token-level block energy ([CalibAtt] key design 1, Eq. (5)).
  *
  * For each row r = (b, h, i) and each key block c of the same (b, h):
- *   energy[r][c] = (1 / 128) * sum over queries t of block i and keys j of block c of P_tj,
+ *   energy[r][c] = (1 / n_i) * sum over queries t of block i and keys j of block c of P_tj,
+ *   n_i = the number of queries block i holds (128 unless it is a partial last block),
  *   P_tj = softmax over ALL lk keys of (q_t . k_j * softmax_scale)
  * so each row sums to 1 (up to rounding). softmax_scale <= 0 means 1 / sqrt(head_dim). The
  * attention matrix is never stored: the kernel makes two passes over the keys (log-sum-exp per

@@ -55,11 +55,11 @@ class Workload:
 
     @property
     def n_q_blocks(self) -> int:
-        return self.lq // BLOCK
+        return -(-self.lq // BLOCK)
 
     @property
     def n_k_blocks(self) -> int:
-        return self.lk // BLOCK
+        return -(-self.lk // BLOCK)
 
     @property
     def rows(self) -> int:
@@ -113,12 +113,14 @@ def make_tensor(w: Workload, tensor: str, device="cpu", seed: int = 0,
     if w.structure == "iid":
         x = torch.randn((w.batch, h, length, d), generator=g, device=dev, dtype=torch.float32)
     elif w.structure == "centroid":
-        nb = length // BLOCK
+        # a partial last block (length not a multiple of 128) takes the first tokens of a
+        # block drawn whole
+        nb = -(-length // BLOCK)
         cent = torch.randn((w.batch, h, nb, 1, d), generator=g, device=dev, dtype=torch.float32)
         cent.mul_(2.0)
         x = torch.randn((w.batch, h, nb, BLOCK, d), generator=g, device=dev, dtype=torch.float32)
         x.mul_(0.5).add_(cent)
-        x = x.view(w.batch, h, length, d)
+        x = x.view(w.batch, h, nb * BLOCK, d)[:, :, :length]
         del cent
     else:
         raise ValueError(f"unknown structure {w.structure!r}")

@@ -120,3 +120,13 @@ def check_token_energy(e_gpu: np.ndarray, e_ref: np.ndarray):
     assert (err <= tol).all(), f"energy mismatch: worst excess {float((err - tol).max()):.3e}"
     assert np.abs(e_gpu.sum(axis=-1) - 1.0).max() <= TOK_ROW_SUM
     assert (e_gpu >= 0).all()
+
+
+def rows_to_tokens(o_rows: np.ndarray, lse_rows: np.ndarray, batch: int, heads: int, lq: int):
+    """Oracle attention per CSR row ([rows, 128, d], [rows, 128]) -> per token ([B, H, lq, d],
+    [B, H, lq]), dropping the slots past the end of a partial last query block."""
+    nqb = -(-lq // BLOCK)
+    d = o_rows.shape[-1]
+    o = o_rows.reshape(batch, heads, nqb * BLOCK, d)[:, :, :lq]
+    lse = lse_rows.reshape(batch, heads, nqb * BLOCK)[:, :, :lq]
+    return o, lse

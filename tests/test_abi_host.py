@@ -134,8 +134,9 @@ def test_select_rejects_bad_arguments(lib):
     assert _select(lib, good, row_ptr=None) == E.DBSP_ERR_INVALID_ARG
     assert _select(lib, good, col_idx=None) == E.DBSP_ERR_INVALID_ARG
     assert _select(lib, good, q=ctypes.c_void_p((1 << 20) + 2)) == E.DBSP_ERR_INVALID_ARG
-    assert _select(lib, _abi.Dims(1, 2, 200, 1024, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
-    assert _select(lib, _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 0, 1024, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 256, 0, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
+    assert _select(lib, _abi.Dims(1, 2, 256, -128, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
     assert _select(lib, _abi.Dims(0, 2, 256, 1024, 128, E.DBSP_BF16)) == E.DBSP_ERR_INVALID_ARG
     assert _select(lib, _abi.Dims(1, 2, 256, 1024, 128, 7)) == E.DBSP_ERR_INVALID_ARG
     assert _select(lib, _abi.Dims(1, 2, 256, 1024, 96, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
@@ -166,7 +167,7 @@ def test_attn_rejects_bad_arguments(lib):
     for kw in ({"q": None}, {"k": None}, {"v": None}, {"rp": None}, {"o": None}, {"ci": None},
                {"cap": -1}, {"odt": 3}, {"scale": float("inf")},
                {"v": ctypes.c_void_p((1 << 20) + 8)},
-               {"dims": _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)}):
+               {"dims": _abi.Dims(1, 2, 256, 0, 128, E.DBSP_BF16)}):
         assert attn(**kw) == E.DBSP_ERR_INVALID_ARG, kw
     assert attn(dims=_abi.Dims(1, 2, 256, 1024, 64, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
     assert attn(dims=_abi.Dims(1, 2, 256, 1024, 32, E.DBSP_F32)) == E.DBSP_ERR_UNSUPPORTED
@@ -181,7 +182,7 @@ def test_energy_calls_reject_bad_arguments(lib):
 
     for kw in ({"q": None}, {"k": None}, {"out": None}, {"scale": float("nan")},
                {"q": ctypes.c_void_p((1 << 20) + 8)}, {"out": ctypes.c_void_p((1 << 20) + 2)},
-               {"dims": _abi.Dims(1, 2, 200, 1024, 128, E.DBSP_BF16)}):
+               {"dims": _abi.Dims(1, 2, 0, 1024, 128, E.DBSP_BF16)}):
         assert energy(**kw) == E.DBSP_ERR_INVALID_ARG, kw
     assert energy(dims=_abi.Dims(1, 2, 256, 1024, 64, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
     assert energy(dims=_abi.Dims(1, 1, 256, 2049 * 128, 128, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
@@ -226,7 +227,7 @@ def test_vote_calls_reject_bad_arguments(lib):
         return lib.dbsp_vote_accumulate(rp, ci, cap, ctypes.byref(dims), counts, None)
 
     for kw in ({"rp": None}, {"counts": None}, {"cap": -1}, {"ci": None},
-               {"dims": _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)}):
+               {"dims": _abi.Dims(1, 2, 256, 0, 128, E.DBSP_BF16)}):
         assert acc(**kw) == E.DBSP_ERR_INVALID_ARG, kw
 
     def sel(dims=good, counts=FAKE, n=4, rho=0.5, rp=FAKE, ci=FAKE, cap=1 << 40, ws=FAKE,
@@ -273,3 +274,19 @@ def test_forced_list_validation(lib):
     assert lib.dbsp_sparse_select_list(FAKE, FAKE, ctypes.byref(dims), ok, 2, E.DBSP_TOPK, 0.5,
                                        -1, 0.0, FAKE, FAKE, 1 << 40, None, None, 0,
                                        None) == E.DBSP_ERR_WORKSPACE
+
+
+def test_partial_block_shapes_are_counted_by_ceil(lib):
+    # lengths that are not multiples of 128 end in a partial block: lk = 1000 -> 8 key blocks,
+    # lq = 200 -> 2 query blocks per head
+    dims = _abi.Dims(1, 2, 200, 1000, 128, _abi.DBSP_BF16)
+    k = ctypes.c_int32()
+    assert lib.dbsp_topk_budget(ctypes.byref(dims), 0.5, _abi.Range(0, 1), _abi.Range(0, 0), -1,
+                                ctypes.byref(k)) == 0
+    assert k.value == 4                                   # ceil(0.5 * 7)
+    nnz = ctypes.c_int64()
+    assert lib.dbsp_select_nnz_bound(ctypes.byref(dims), _abi.DBSP_MASS, 0.9, _abi.Range(0, 1),
+                                     _abi.Range(0, 0), -1, ctypes.byref(nnz)) == 0
+    assert nnz.value == 2 * 2 * 8
+    ws = ctypes.c_uint64()
+    assert lib.dbsp_select_energy_workspace_bytes(ctypes.byref(dims), ctypes.byref(ws)) == 0

@@ -83,9 +83,8 @@ def full_check_small(w: Workload, seed=3, inputs=None, score_scale=None):
                                    s_ref.reshape(-1, nkb), forced, tol)
         say(f"  rows differing from the oracle's own masks (near ties only): {ndiff}")
     o_ref, lse_ref = oracle.attention_rows(qh, kh, vh, rp, ci, scale=1.0 / math.sqrt(w.head_dim))
-    o_g = P.host(o).reshape(o_ref.shape)
-    l_g = P.host(lse).reshape(lse_ref.shape)
-    mx, mean = P.check_attention(o_g, l_g, o_ref, lse_ref, w.dtype == "bf16")
+    o_ref, lse_ref = P.rows_to_tokens(o_ref, lse_ref, w.batch, w.heads, w.lq)
+    mx, mean = P.check_attention(P.host(o), P.host(lse), o_ref, lse_ref, w.dtype == "bf16")
     say(f"  O max err {mx:.2e} mean {mean:.2e}; nnz {int(rp[-1])}")
     return idx, o, lse
 
@@ -281,3 +280,48 @@ def test_forced_list(mode):
     assert n == idx_l.nnz()
     assert torch.equal(idx_r.row_ptr, idx_l.row_ptr)
     assert torch.equal(idx_r.col_idx[:n], idx_l.col_idx[:n])
+
+
+
+PARTIAL = {
+    # lengths that are not multiples of 128: partial last query and key blocks
+    "bf16 topk": small_variants()["final_small"].with_(name="partial_topk",
+                                                       lq=17 * BLOCK - 37, lk=70 * BLOCK - 51),
+    "bf16 mass": small_variants()["dit_mass_small"].with_(name="partial_mass",
+                                                          lq=19 * BLOCK - 48, lk=19 * BLOCK - 48),
+    "bf16 clip1": small_variants()["clip1_small"].with_(name="partial_clip1",
+                                                        lq=11 * BLOCK - 1, lk=23 * BLOCK - 127),
+    "fp32 toy": WORKLOADS["toy"].with_(name="partial_toy", lq=1000, lk=900),
+    "bf16 one short block": small_variants()["star_mid_small"].with_(
+        name="partial_tiny", lq=77, lk=100, text=(0, 1)),
+}
+
+
+@pytest.mark.parametrize("name", list(PARTIAL))
+def test_partial_blocks(name):
+    full_check_small(PARTIAL[name], seed=31)
+
+
+def test_partial_blocks_energy_and_anchor():
+    m = dbsp()
+    w = PARTIAL["bf16 mass"]
+    say(f"case partial energy lq={w.lq} lk={w.lk}")
+    q, k, v = make_qkv(w, device="cuda", seed=32)
+    e, lse = m.block_energy(q, k, return_lse=True)
+    torch.cuda.synchronize()
+    qh, kh = P.host(q), P.host(k)
+    P.check_token_energy(P.host(e), oracle.block_energy_rows(qh, kh, rows=range(w.rows)))
+    assert np.abs(P.host(lse) - oracle.attention_dense(qh, kh, kh)[1]).max() <= P.TOK_LSE
+    wf = PARTIAL["fp32 toy"]
+    say(f"case partial energy fp32 lq={wf.lq} lk={wf.lk}")
+    qf, kf, _ = make_qkv(wf, device="cuda", seed=33)
+    ef = m.block_energy(qf, kf)
+    torch.cuda.synchronize()
+    P.check_token_energy(P.host(ef), oracle.block_energy_rows(P.host(qf), P.host(kf),
+                                                              rows=range(wf.rows)))
+    # anchor path with keys ending in a partial block
+    say("case partial anchor")
+    o, l2 = m.anchor_attn_fwd(q, k, v, 3, 7, 100, 2, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.anchor_attention(qh, kh, P.host(v), 3, 7, 100, 2)
+    P.check_attention(P.host(o), P.host(l2), o_ref, l_ref, bf16_inputs=True)
