@@ -24,7 +24,7 @@ from ._abi import DBSP_BLOCK, DbspError
 
 __all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "topk_budget", "select_nnz_bound",
            "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
-           "MaskVote", "anchor_attn_fwd",
+           "MaskVote", "anchor_attn_fwd", "to_intervals", "from_intervals",
            "DbspError", "DBSP_BLOCK", "version"]
 
 
@@ -378,3 +378,56 @@ def anchor_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, frames: i
                                   _ptr(workspace), workspace.numel(), _stream(q.device))
     _abi.check(st, "dbsp_anchor_attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def _skiplist_workspace(dims, device):
+    n = ctypes.c_uint64()
+    _abi.check(_abi.load().dbsp_skiplist_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)),
+               "dbsp_skiplist_workspace_bytes")
+    return torch.empty(max(n.value, 1), dtype=torch.uint8, device=device)
+
+
+def _index_dims(index: BlockIndex, batch: int, heads: int) -> _abi.Dims:
+    rows = index.row_ptr.numel() - 1
+    if rows % (batch * heads):
+        raise ValueError("index rows are not a multiple of batch * heads")
+    nqb = rows // (batch * heads)
+    return _abi.Dims(batch, heads, nqb * DBSP_BLOCK, index.n_k_blocks * DBSP_BLOCK, 128,
+                     _abi.DBSP_BF16)
+
+
+def to_intervals(index: BlockIndex, batch: int = 1, heads: int = 1):
+    """Encode a CSR skip list as maximal runs of key blocks: (iv_ptr [rows + 1] int32, iv
+    [capacity, 2] int32 [start, end) pairs; the first iv_ptr[-1] are used)."""
+    dims = _index_dims(index, batch, heads)
+    dev = index.row_ptr.device
+    rows = index.row_ptr.numel() - 1
+    cap = rows * ((index.n_k_blocks + 1) // 2)
+    iv_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    iv = torch.empty((max(cap, 1), 2), dtype=torch.int32, device=dev)
+    ws = _skiplist_workspace(dims, dev)
+    st = _abi.load().dbsp_csr_to_intervals(_ptr(index.row_ptr), _ptr(index.col_idx),
+                                           index.col_idx.numel(), ctypes.byref(dims),
+                                           _ptr(iv_ptr), _ptr(iv), iv.shape[0], _ptr(ws),
+                                           ws.numel(), _stream(dev))
+    _abi.check(st, "dbsp_csr_to_intervals")
+    return iv_ptr, iv
+
+
+def from_intervals(iv_ptr: torch.Tensor, iv: torch.Tensor, n_q_blocks: int, n_k_blocks: int,
+                   batch: int = 1, heads: int = 1) -> BlockIndex:
+    """Decode an interval skip list into the CSR the attention call reads."""
+    dims = _abi.Dims(batch, heads, n_q_blocks * DBSP_BLOCK, n_k_blocks * DBSP_BLOCK, 128,
+                     _abi.DBSP_BF16)
+    dev = iv_ptr.device
+    rows = batch * heads * n_q_blocks
+    if iv_ptr.numel() != rows + 1:
+        raise ValueError("iv_ptr has the wrong length")
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(rows * n_k_blocks, 1), dtype=torch.int32, device=dev)
+    ws = _skiplist_workspace(dims, dev)
+    st = _abi.load().dbsp_intervals_to_csr(_ptr(iv_ptr), _ptr(iv), iv.shape[0],
+                                           ctypes.byref(dims), _ptr(row_ptr), _ptr(col_idx),
+                                           col_idx.numel(), _ptr(ws), ws.numel(), _stream(dev))
+    _abi.check(st, "dbsp_intervals_to_csr")
+    return BlockIndex(row_ptr, col_idx, n_q_blocks, n_k_blocks, None)

@@ -61,6 +61,9 @@ SIGNATURES = {
     "dbsp_vote_accumulate": (_i32, [_vp, _vp, _i64, _PDims, _vp, _vp]),
     "dbsp_vote_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
     "dbsp_vote_select": (_i32, [_vp, _PDims, _i32, _f64, _vp, _vp, _i64, _vp, _u64, _vp]),
+    "dbsp_skiplist_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
+    "dbsp_csr_to_intervals": (_i32, [_vp, _vp, _i64, _PDims, _vp, _vp, _i64, _vp, _u64, _vp]),
+    "dbsp_intervals_to_csr": (_i32, [_vp, _vp, _i64, _PDims, _vp, _vp, _i64, _vp, _u64, _vp]),
     "dbsp_anchor_workspace_bytes": (_i32, [_PDims, _i32, _i32, _i32, _i32, _i32,
                                            ctypes.POINTER(_u64)]),
     "dbsp_anchor_attn_fwd": (_i32, [_vp, _vp, _vp, _PDims, _i32, _i32, _i32, _i32, _f32, _vp,

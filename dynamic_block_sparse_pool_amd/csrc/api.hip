@@ -605,4 +605,51 @@ int32_t dbsp_anchor_attn_fwd(const void* q, const void* k, const void* v, const 
   return DBSP_OK;
 }
 
+int32_t dbsp_skiplist_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes) {
+  if (!shape_ok(dims) || !bytes) return DBSP_ERR_INVALID_ARG;
+  *bytes = align256((uint64_t)rows_of(dims) * sizeof(int32_t));
+  return DBSP_OK;
+}
+
+int32_t dbsp_csr_to_intervals(const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_capacity, const dbsp_dims* dims, int32_t* iv_ptr,
+                              int32_t* iv, int64_t iv_capacity, void* workspace,
+                              uint64_t workspace_bytes, void* stream) {
+  if (!shape_ok(dims) || !row_ptr || !iv_ptr || !iv) return DBSP_ERR_INVALID_ARG;
+  if (col_capacity < 0 || (col_capacity > 0 && !col_idx) || iv_capacity < 0)
+    return DBSP_ERR_INVALID_ARG;
+  const int64_t nkb = nkb_of(dims);
+  // a row holds at most ceil(nkb / 2) maximal runs of in-range blocks
+  if (iv_capacity < rows_of(dims) * ((nkb + 1) / 2)) return DBSP_ERR_CAPACITY;
+  if (!workspace || workspace_bytes < (uint64_t)rows_of(dims) * sizeof(int32_t) ||
+      ((uintptr_t)workspace & 255u))
+    return DBSP_ERR_WORKSPACE;
+  if (dbsp::launch_csr_to_intervals(row_ptr, col_idx, col_capacity, (int)nkb, rows_of(dims),
+                                    iv_ptr, iv, iv_capacity, static_cast<int32_t*>(workspace),
+                                    static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
+int32_t dbsp_intervals_to_csr(const int32_t* iv_ptr, const int32_t* iv, int64_t iv_capacity,
+                              const dbsp_dims* dims, int32_t* row_ptr, int32_t* col_idx,
+                              int64_t col_capacity, void* workspace, uint64_t workspace_bytes,
+                              void* stream) {
+  if (!shape_ok(dims) || !iv_ptr || !row_ptr || !col_idx) return DBSP_ERR_INVALID_ARG;
+  if (iv_capacity < 0 || (iv_capacity > 0 && !iv) || col_capacity < 0)
+    return DBSP_ERR_INVALID_ARG;
+  const int64_t nkb = nkb_of(dims);
+  const int64_t bound = rows_of(dims) * nkb;  // disjoint intervals of a row cover at most nkb
+  if (bound > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  if (col_capacity < bound) return DBSP_ERR_CAPACITY;
+  if (!workspace || workspace_bytes < (uint64_t)rows_of(dims) * sizeof(int32_t) ||
+      ((uintptr_t)workspace & 255u))
+    return DBSP_ERR_WORKSPACE;
+  if (dbsp::launch_intervals_to_csr(iv_ptr, iv, iv_capacity, (int)nkb, rows_of(dims), row_ptr,
+                                    col_idx, col_capacity, static_cast<int32_t*>(workspace),
+                                    static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
+}
+
 }  // extern "C"

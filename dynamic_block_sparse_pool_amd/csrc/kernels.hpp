@@ -102,6 +102,15 @@ hipError_t launch_retained_mass(const float* energy, const int32_t* row_ptr,
 hipError_t launch_select_energy(const SelectArgs& a, const float* energy, hipStream_t stream);
 // row_ptr / col_idx from the per-row counts and kept bitmasks in a.counts / a.masks
 hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream);
+// a.row_ptr = exclusive prefix of a.counts over a.n_rows rows (row_ptr[n_rows] = total)
+hipError_t launch_scan_counts(const SelectArgs& a, hipStream_t stream);
+hipError_t launch_csr_to_intervals(const int32_t* row_ptr, const int32_t* col_idx,
+                                   int64_t col_capacity, int nkb, int64_t rows, int32_t* iv_ptr,
+                                   int32_t* iv, int64_t iv_capacity, int32_t* counts,
+                                   hipStream_t stream);
+hipError_t launch_intervals_to_csr(const int32_t* iv_ptr, const int32_t* iv, int64_t iv_capacity,
+                                   int nkb, int64_t rows, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, int32_t* counts, hipStream_t stream);
 hipError_t launch_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx,
                                   int64_t col_capacity, int nkb, int64_t rows, int32_t* counts,
                                   hipStream_t stream);

@@ -560,9 +560,13 @@ __global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const 
   select_mass_probs<S>(a, p, row, lane);
 }
 
-hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream) {
+hipError_t launch_scan_counts(const SelectArgs& a, hipStream_t stream) {
   scan_counts_kernel<<<1, 1024, 0, stream>>>(a.counts, a.row_ptr, a.n_rows);
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream) {
+  hipError_t err = launch_scan_counts(a, stream);
   if (err != hipSuccess) return err;
   fill_csr_kernel<<<(unsigned)((a.n_rows + 3) / 4), 256, 0, stream>>>(
       a.masks, a.row_ptr, a.col_idx, a.n_rows, a.words, a.col_capacity);

@@ -17,6 +17,8 @@
  *                         masks of several calibration inputs -> one static CSR by vote.
  *   dbsp_anchor_attn_fwd  the alternative path of spatially repeating heads: attention for a few
  *                         anchor rows per frame, broadcast to the nearest rows.
+ *   dbsp_csr_to_intervals, dbsp_intervals_to_csr
+ *                         the skip list as contiguous key-block intervals, and back.
  *
  * What the calls compute follows two pages:
  *   [SparSTAR] "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video Synthesis", in the
@@ -281,6 +283,32 @@ int32_t dbsp_vote_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
 int32_t dbsp_vote_select(const int32_t* counts, const dbsp_dims* dims, int32_t n_inputs, double rho,
                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                          void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Interval skip list ([CalibAtt] key design 4: the mask of each query block is stored as the
+ * contiguous intervals of key blocks it needs, loaded read-only before generation).
+ *
+ * dbsp_csr_to_intervals encodes a CSR (as written by dbsp_sparse_select, dbsp_select_energy or
+ * dbsp_vote_select: ascending, distinct entries) as maximal runs: iv_ptr [rows + 1] (device
+ * int32, exclusive prefix of the run counts) and iv [n_runs][2] (device int32 pairs
+ * [start, end) of key blocks, ascending). Entries outside [0, lk / 128) are skipped.
+ * iv_capacity (pairs) must be at least rows * ceil((lk / 128) / 2), the most runs a mask can
+ * have.
+ * dbsp_intervals_to_csr decodes intervals (clipped to [0, lk / 128); those of a row must not
+ * overlap) into row_ptr / col_idx; col_capacity must be at least rows * (lk / 128).
+ * Both take a workspace of at least dbsp_skiplist_workspace_bytes (per-row counts), 256-byte
+ * aligned. Errors: DBSP_ERR_INVALID_ARG for null pointers, a bad shape or a negative
+ * capacity; DBSP_ERR_CAPACITY below the bounds above; DBSP_ERR_WORKSPACE.
+ */
+int32_t dbsp_skiplist_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
+int32_t dbsp_csr_to_intervals(const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t col_capacity, const dbsp_dims* dims, int32_t* iv_ptr,
+                              int32_t* iv, int64_t iv_capacity, void* workspace,
+                              uint64_t workspace_bytes, void* stream);
+int32_t dbsp_intervals_to_csr(const int32_t* iv_ptr, const int32_t* iv, int64_t iv_capacity,
+                              const dbsp_dims* dims, int32_t* row_ptr, int32_t* col_idx,
+                              int64_t col_capacity, void* workspace, uint64_t workspace_bytes,
+                              void* stream);
 
 /*
  * Anchor-row attention for spatially repeating heads ([CalibAtt] key design 3, spatial

@@ -19,7 +19,7 @@ Every function cites the passage it follows by page title and section. Readings 
 pages are silent are listed in the docstrings of the functions that make them.
 """
 from .select import (BLOCK, MASS_BITS, block_scores, block_softmax, forced_blocks, mass_threshold_units,
-                     mass_units, n_blocks, pool, select_mass, select_topk, sparse_select, to_csr,
+                     mass_units, n_blocks, pool, select_mass, select_topk, sparse_select, to_csr, to_intervals,
                      topk_budget)
 from .attention import attention_dense, attention_masked, attention_rows
 from .energy import block_energy_rows, retained_mass, token_upper_bound
@@ -29,6 +29,7 @@ from .anchor import anchor_attention, anchor_rows, nearest_anchor
 __all__ = [
     "BLOCK", "MASS_BITS", "n_blocks", "pool", "block_scores", "block_softmax", "forced_blocks",
     "topk_budget", "select_topk", "mass_units", "mass_threshold_units", "select_mass", "to_csr",
+    "to_intervals",
     "sparse_select", "attention_rows", "attention_masked", "attention_dense", "block_energy_rows",
     "token_upper_bound", "retained_mass", "vote_masks", "anchor_rows", "nearest_anchor",
     "anchor_attention",

@@ -194,6 +194,25 @@ def to_csr(kept) -> Tuple[np.ndarray, np.ndarray]:
     return row_ptr, col_idx
 
 
+def to_intervals(kept) -> Tuple[np.ndarray, np.ndarray]:
+    """[CalibAtt] key design 4: the skip list stores, per query block, the contiguous runs of
+    key blocks it needs. kept [rows, nKB] -> (iv_ptr [rows+1] int64, exclusive prefix of the run
+    counts; iv [n_runs, 2] int64 half-open [start, end) block ranges, ascending and maximal
+    (two runs of a row never touch))."""
+    kept = np.asarray(kept, dtype=bool)
+    kept = kept.reshape(-1, kept.shape[-1])
+    starts, ptr = [], [0]
+    for row in kept:
+        padded = np.concatenate([[False], row, [False]]).astype(np.int8)
+        edge = np.diff(padded)
+        b = np.nonzero(edge == 1)[0]
+        e = np.nonzero(edge == -1)[0]
+        starts.extend(zip(b.tolist(), e.tolist()))
+        ptr.append(ptr[-1] + b.size)
+    iv = np.array(starts, dtype=np.int64).reshape(-1, 2)
+    return np.array(ptr, dtype=np.int64), iv
+
+
 def sparse_select(q, k, text: Tuple[int, int], extra: Tuple[int, int], mode: str, param: float,
                   score_scale: Optional[float] = None, topk_override: Optional[int] = None,
                   block: int = BLOCK) -> dict:

@@ -290,3 +290,29 @@ def test_partial_block_shapes_are_counted_by_ceil(lib):
     assert nnz.value == 2 * 2 * 8
     ws = ctypes.c_uint64()
     assert lib.dbsp_select_energy_workspace_bytes(ctypes.byref(dims), ctypes.byref(ws)) == 0
+
+
+def test_skiplist_calls_reject_bad_arguments(lib):
+    E = _abi
+    dims = _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)   # 4 rows, 8 key blocks
+
+    def enc(rp=FAKE, ci=FAKE, cap=16, ivp=FAKE, iv=FAKE, ivcap=16, ws=FAKE, wsb=1 << 20):
+        return lib.dbsp_csr_to_intervals(rp, ci, cap, ctypes.byref(dims), ivp, iv, ivcap, ws, wsb,
+                                         None)
+
+    for kw in ({"rp": None}, {"ivp": None}, {"iv": None}, {"ci": None}, {"cap": -1},
+               {"ivcap": -1}):
+        assert enc(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    assert enc(ivcap=15) == E.DBSP_ERR_CAPACITY          # 4 rows x ceil(8 / 2) runs
+    assert enc(ws=None) == E.DBSP_ERR_WORKSPACE
+    assert enc(wsb=8) == E.DBSP_ERR_WORKSPACE
+
+    def dec(ivp=FAKE, iv=FAKE, ivcap=16, rp=FAKE, ci=FAKE, cap=32, ws=FAKE, wsb=1 << 20):
+        return lib.dbsp_intervals_to_csr(ivp, iv, ivcap, ctypes.byref(dims), rp, ci, cap, ws, wsb,
+                                         None)
+
+    for kw in ({"ivp": None}, {"rp": None}, {"ci": None}, {"iv": None}, {"ivcap": -1},
+               {"cap": -1}):
+        assert dec(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    assert dec(cap=31) == E.DBSP_ERR_CAPACITY             # 4 rows x 8 blocks
+    assert dec(ws=ctypes.c_void_p((1 << 20) + 8)) == E.DBSP_ERR_WORKSPACE

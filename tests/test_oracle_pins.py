@@ -583,3 +583,27 @@ def test_anchor_path_exact_on_repeating_rows():
     o_d, l_d = _dense(q, k, v)
     np.testing.assert_allclose(o, o_d, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l, l_d, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- interval skip list
+
+def test_intervals_hand_example_and_round_trip():
+    kept = np.array([[1, 1, 0, 1, 0, 0, 1, 1],
+                     [0, 0, 0, 0, 0, 0, 0, 0],
+                     [1, 1, 1, 1, 1, 1, 1, 1],
+                     [0, 1, 0, 1, 0, 1, 0, 1]], dtype=bool)
+    ptr, iv = oracle.to_intervals(kept)
+    assert ptr.tolist() == [0, 3, 3, 4, 8]
+    assert iv.tolist() == [[0, 2], [3, 4], [6, 8], [0, 8], [1, 2], [3, 4], [5, 6], [7, 8]]
+    rng = np.random.default_rng(43)
+    for density in (0.05, 0.5, 0.95):
+        kept = rng.random((9, 77)) < density
+        ptr, iv = oracle.to_intervals(kept)
+        back = np.zeros_like(kept)
+        for r in range(kept.shape[0]):
+            for s_, e_ in iv[ptr[r]:ptr[r + 1]]:
+                assert s_ < e_
+                back[r, s_:e_] = True
+            runs = iv[ptr[r]:ptr[r + 1]]
+            assert (runs[1:, 0] > runs[:-1, 1]).all()      # maximal: runs never touch
+        np.testing.assert_array_equal(back, kept)
