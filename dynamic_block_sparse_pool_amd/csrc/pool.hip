@@ -48,12 +48,19 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
   const int row0 = t / kChunks;
 
   u32x4 raw[kPasses];
+  if (valid == kBlock) {  // uniform: a whole block, unguarded loads
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = row0 + p * kRowsPerPass;
-    raw[p] = row < valid ? __builtin_nontemporal_load(
-                               reinterpret_cast<const u32x4*>(src + (int64_t)row * D) + chunk)
-                         : u32x4{0u, 0u, 0u, 0u};
+    for (int p = 0; p < kPasses; ++p)
+      raw[p] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(src + (int64_t)(row0 + p * kRowsPerPass) * D) + chunk);
+  } else {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int row = row0 + p * kRowsPerPass;
+      raw[p] = row < valid ? __builtin_nontemporal_load(
+                                 reinterpret_cast<const u32x4*>(src + (int64_t)row * D) + chunk)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   float acc[kVec];

@@ -59,8 +59,9 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
 // Callers pass 0 <= c < nkb <= 2048, so the word index is in range; it is uniform across a
 // wave (c = 64 e + lane), so the word comes from the kernel arguments through a scalar load.
 __device__ __forceinline__ bool is_forced(int c, const SelectArgs& a) {
-  if (a.forced_by_words) return (a.forced_words[c >> 6] >> (c & 63)) & 1ull;
-  return (c >= a.t0 && c < a.t1) || (c >= a.e0 && c < a.e1);
+  const bool in_ranges = (c >= a.t0 && c < a.t1) || (c >= a.e0 && c < a.e1);
+  const bool in_words = (a.forced_words[c >> 6] >> (c & 63)) & 1ull;
+  return a.forced_by_words ? in_words : in_ranges;
 }
 
 // The threshold lies between the smallest and largest candidate key, so it shares their
@@ -120,22 +121,42 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
       for (int w = 0; w < 4; ++w) acc[w] += __uint_as_float(raw[w]);
     }
   };
+  if (valid0 == kBlock && valid1 == kBlock) {  // uniform: whole blocks, unguarded loads
 #pragma unroll 1
-  for (int b = 0; b < kLoads; b += kBatch) {
-    u32x4 raw0[kBatch], raw1[kBatch];
+    for (int b = 0; b < kLoads; b += kBatch) {
+      u32x4 raw0[kBatch], raw1[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int row = (b + i) * kRowsPerLoad + r0;
-      const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
-      raw0[i] = row < valid0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off))
-                             : u32x4{0u, 0u, 0u, 0u};
-      raw1[i] = row < valid1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off))
-                             : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
+        raw0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off));
+        raw1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off));
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        add(acc0, raw0[i]);
+        add(acc1, raw1[i]);
+      }
     }
+  } else {  // a partial last block: rows past its end are not read
+#pragma unroll 1
+    for (int b = 0; b < kLoads; b += kBatch) {
+      u32x4 raw0[kBatch], raw1[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      add(acc0, raw0[i]);
-      add(acc1, raw1[i]);
+      for (int i = 0; i < kBatch; ++i) {
+        const int row = (b + i) * kRowsPerLoad + r0;
+        const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
+        raw0[i] = row < valid0
+                      ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off))
+                      : u32x4{0u, 0u, 0u, 0u};
+        raw1[i] = row < valid1
+                      ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off))
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        add(acc0, raw0[i]);
+        add(acc1, raw1[i]);
+      }
     }
   }
 #pragma unroll
