@@ -519,31 +519,54 @@ __global__ __launch_bounds__(64 * kWaves) void score_select_kernel(SelectArgs a,
   }
 }
 
-// Exclusive prefix sum of the per-row counts into row_ptr (single workgroup of 1024 threads).
+// Exclusive prefix sum of the per-row counts into row_ptr (one workgroup of 1024 threads).
+// Passes of 8192 rows: thread t takes rows 8 t .. 8 t + 7 of the pass (all loads issued first),
+// adds them, the 1024 thread totals are scanned (DPP wave scans, then the 16 wave totals), and
+// every thread writes its 8 exclusive prefixes. Counts are small (at most 2048 per row), so
+// int32 prefixes suffice: the host rejects an nnz bound above INT32_MAX.
 __global__ __launch_bounds__(1024) void scan_counts_kernel(const int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ row_ptr,
                                                            int64_t rows) {
-  __shared__ int64_t part[1024];
+  constexpr int kPer = 8;
+  constexpr int64_t kPass = 1024 * kPer;
+  __shared__ uint32_t wave_tot[16];
   const int t = threadIdx.x;
-  const int64_t seg = (rows + 1023) / 1024;
-  const int64_t b = t * seg;
-  const int64_t e = (b + seg < rows) ? b + seg : rows;
-  int64_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += counts[i];
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int64_t v = (t >= off) ? part[t - off] : 0;
+  const int lane = t & 63, wave = t >> 6;
+  uint32_t carry = 0;  // sum of all earlier passes
+  for (int64_t base = 0; base < rows; base += kPass) {
+    const int64_t r0 = base + (int64_t)t * kPer;
+    int32_t c[kPer];
+    if (r0 + kPer <= rows) {  // 32 contiguous bytes per thread (counts is 256-byte aligned)
+      const u32x4 a = load_u32x4(counts + r0), b = load_u32x4(counts + r0 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = (int32_t)a[i];
+        c[4 + i] = (int32_t)b[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) c[i] = r0 + i < rows ? counts[r0 + i] : 0;
+    }
+    uint32_t own = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) own += (uint32_t)c[i];
+    const uint32_t incl = wave_prefix_sum_u32(own);  // within the wave
+    if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    part[t] += v;
-    __syncthreads();
+    uint32_t before = carry;
+    for (int i = 0; i < wave; ++i) before += wave_tot[i];
+    uint32_t pass_total = 0;
+    for (int i = 0; i < 16; ++i) pass_total += wave_tot[i];
+    uint32_t run = before + incl - own;  // exclusive prefix of this thread's first row
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (r0 + i < rows) row_ptr[r0 + i] = (int32_t)run;
+      run += (uint32_t)c[i];
+    }
+    carry += pass_total;
+    __syncthreads();  // wave_tot is rewritten by the next pass
   }
-  int64_t run = part[t] - s;  // exclusive
-  for (int64_t i = b; i < e; ++i) {
-    row_ptr[i] = (int32_t)run;
-    run += counts[i];
-  }
-  if (t == 1023) row_ptr[rows] = (int32_t)part[1023];
+  if (t == 0) row_ptr[rows] = (int32_t)carry;
 }
 
 // Expand per-row bitmasks into ascending col_idx (one wave per row).

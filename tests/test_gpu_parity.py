@@ -325,3 +325,13 @@ def test_partial_blocks_energy_and_anchor():
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.anchor_attention(qh, kh, P.host(v), 3, 7, 100, 2)
     P.check_attention(P.host(o), P.host(l2), o_ref, l_ref, bf16_inputs=True)
+
+
+def test_batch_two():
+    # two batch entries: rows (b * H + h) * nQB + i, per-(b, h) pooling and K/V bases
+    w = small_variants()["final_small"].with_(name="batch2", batch=2, heads=3,
+                                              lq=7 * BLOCK, lk=(4 + 20) * BLOCK)
+    full_check_small(w, seed=61)
+    wm = small_variants()["dit_mass_small"].with_(name="batch2_mass", batch=2,
+                                                  lq=5 * BLOCK - 3, lk=9 * BLOCK - 100)
+    full_check_small(wm, seed=62)
