@@ -96,6 +96,22 @@ def _check_device_tensor(name: str, t: torch.Tensor) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_view(name: str, t: torch.Tensor) -> None:
+    """A 4-D GPU view whose last dimension is contiguous (other strides are passed through)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be a [batch, heads, L, head_dim] view with contiguous "
+                         "head_dim")
+
+
+def _strides(t: torch.Tensor):
+    """None for a contiguous tensor, else its [batch, heads, L] element strides."""
+    if t.is_contiguous():
+        return None
+    return _abi.Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
 def topk_budget(n_k_blocks: int, density: float, text_blocks=(0, 0), dense_extra_blocks=(0, 0),
                 topk_override: int = -1) -> int:
     """K, the number of non-forced key blocks Top-K keeps per row (host-only query)."""
@@ -139,8 +155,8 @@ class SelectPlan:
         # an explicit forced list replaces the two ranges
         self.forced = (None if forced_blocks is None else
                        (ctypes.c_int32 * len(forced_blocks))(*[int(c) for c in forced_blocks]))
-        _check_device_tensor("q", q)
-        _check_device_tensor("k", k)
+        _check_view("q", q)
+        _check_view("k", k)
         self.dims = _dims(q, k)
         self.mode = _abi.DBSP_TOPK if density is not None else _abi.DBSP_MASS
         self.param = float(density if density is not None else mass)
@@ -175,9 +191,21 @@ class SelectPlan:
                 self.dims.batch, self.dims.heads, self.dims.lq, self.dims.lk, self.dims.head_dim,
                 self.dims.dtype):
             raise ValueError("q / k shape or dtype differs from the plan")
-        _check_device_tensor("q", q)
-        _check_device_tensor("k", k)
-        if self.forced is None:
+        _check_view("q", q)
+        _check_view("k", k)
+        qs, ks = _strides(q), _strides(k)
+        if (qs is not None or ks is not None) and self.forced is not None:
+            raise ValueError("strided q / k with a forced list is not supported; pass ranges")
+        if qs is not None or ks is not None:
+            qs = qs or _abi.Strides(q.stride(0), q.stride(1), q.stride(2))
+            ks = ks or _abi.Strides(k.stride(0), k.stride(1), k.stride(2))
+            st = _abi.load().dbsp_sparse_select_strided(
+                _ptr(q), ctypes.byref(qs), _ptr(k), ctypes.byref(ks), ctypes.byref(self.dims),
+                self.text, self.extra, self.mode, self.param, self.topk_override,
+                self.score_scale, _ptr(self.row_ptr), _ptr(self.col_idx), self.col_idx.numel(),
+                _ptr(self.scores), _ptr(self.workspace), self.workspace.numel(),
+                _stream(q.device))
+        elif self.forced is None:
             st = _abi.load().dbsp_sparse_select(
                 _ptr(q), _ptr(k), ctypes.byref(self.dims), self.text, self.extra, self.mode,
                 self.param, self.topk_override, self.score_scale, _ptr(self.row_ptr),
@@ -213,7 +241,7 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
     """Forward attention of every query block over the tokens of its kept key blocks only.
     Returns O (and lse if return_lse)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_device_tensor(name, t)
+        _check_view(name, t)
     dims = _dims(q, k)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
@@ -225,14 +253,23 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
     odt = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
     if out is None:
         out = torch.empty(q.shape, dtype=odt, device=q.device)
-    elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
-        raise ValueError("out has the wrong shape, dtype or layout")
+    elif out.shape != q.shape or out.dtype != odt:
+        raise ValueError("out has the wrong shape or dtype")
+    _check_view("out", out)
     if return_lse and lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    st = _abi.load().dbsp_sparse_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), _ptr(index.row_ptr), _ptr(index.col_idx),
-        index.col_idx.numel(), float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
-        _stream(q.device))
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        st = _abi.load().dbsp_sparse_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), _ptr(index.row_ptr),
+            _ptr(index.col_idx), index.col_idx.numel(), float(softmax_scale), _ptr(out),
+            _dtype_code(out), _ptr(lse), _stream(q.device))
+    else:
+        ss = [_abi.Strides(t.stride(0), t.stride(1), t.stride(2)) for t in (q, k, v, out)]
+        st = _abi.load().dbsp_sparse_attn_fwd_strided(
+            _ptr(q), ctypes.byref(ss[0]), _ptr(k), ctypes.byref(ss[1]), _ptr(v),
+            ctypes.byref(ss[2]), ctypes.byref(dims), _ptr(index.row_ptr), _ptr(index.col_idx),
+            index.col_idx.numel(), float(softmax_scale), _ptr(out), ctypes.byref(ss[3]),
+            _dtype_code(out), _ptr(lse), _stream(q.device))
     _abi.check(st, "dbsp_sparse_attn_fwd")
     return (out, lse) if return_lse else out
 

@@ -34,9 +34,14 @@ class Dims(ctypes.Structure):
                 ("lk", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
 _i32, _i64, _u64, _f32, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_double
 _vp = ctypes.c_void_p
 _PDims = ctypes.POINTER(Dims)
+_PStr = ctypes.POINTER(Strides)
 
 # name -> (restype, argtypes); the order of arguments follows include/dbsp.h
 SIGNATURES = {
@@ -49,6 +54,11 @@ SIGNATURES = {
                                   _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _PDims, _vp, _vp, _i64, _f32, _vp, _i32, _vp,
                                     _vp]),
+    "dbsp_sparse_select_strided": (_i32, [_vp, _PStr, _vp, _PStr, _PDims, Range, Range, _i32,
+                                          _f64, _i32, _f32, _vp, _vp, _i64, _vp, _vp, _u64,
+                                          _vp]),
+    "dbsp_sparse_attn_fwd_strided": (_i32, [_vp, _PStr, _vp, _PStr, _vp, _PStr, _PDims, _vp, _vp,
+                                            _i64, _f32, _vp, _PStr, _i32, _vp, _vp]),
     "dbsp_sparse_select_list": (_i32, [_vp, _vp, _PDims, _vp, _i32, _i32, _f64, _i32, _f32,
                                        _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_select_nnz_bound_list": (_i32, [_PDims, _i32, _f64, _vp, _i32, _i32,

@@ -138,6 +138,12 @@ hipError_t launch_anchor(const AnchorArgs& a, int head_dim, bool bf16, hipStream
   at.nkb = a.nkb;
   at.lq = g.la_pad;
   at.lk = a.lk;
+  // every buffer is contiguous per (batch, head) pair bh, so the pairs act as one batch axis
+  at.heads = 1;
+  at.qs = Strides{g.la_pad * head_dim, 0, head_dim};
+  at.ks = Strides{a.lk * head_dim, 0, head_dim};
+  at.vs = at.ks;
+  at.os = at.qs;
   at.rows = rows_a;
   at.scale_log2 = a.scale_log2;
   at.o = a.oa;

@@ -239,6 +239,27 @@ WorkspaceLayout energy_select_layout(const dbsp_dims* d) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Strides of a contiguous [batch, heads, len, head_dim] tensor.
+dbsp::Strides contiguous(const dbsp_dims* d, int64_t len) {
+  return dbsp::Strides{(int64_t)d->heads * len * d->head_dim, len * d->head_dim,
+                       (int64_t)d->head_dim};
+}
+
+// Caller strides: non-negative, every row 16-byte aligned (as the base pointer must be), and
+// for written tensors rows that do not overlap within a head.
+bool strides_ok(const dbsp_strides* s, const dbsp_dims* d, bool written) {
+  if (!s) return false;
+  const int64_t elt = d->dtype == DBSP_BF16 ? 2 : 4;
+  if (s->batch < 0 || s->head < 0 || s->token < 0) return false;
+  if ((s->batch * elt) % 16 || (s->head * elt) % 16 || (s->token * elt) % 16) return false;
+  if (written && s->token < d->head_dim) return false;
+  return true;
+}
+
+dbsp::Strides to_strides(const dbsp_strides* s) {
+  return dbsp::Strides{s->batch, s->head, s->token};
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,6 +308,7 @@ int32_t dbsp_select_workspace_bytes(const dbsp_dims* dims, int32_t mode, uint64_
 }
 
 static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims* dims,
+                                  const dbsp_strides* q_strides, const dbsp_strides* k_strides,
                                   const ForcedSet* fs_in, dbsp_range text_blocks,
                                   dbsp_range dense_extra_blocks, int32_t mode,
                                   double density_or_mass, int32_t topk_override, float score_scale,
@@ -298,9 +320,14 @@ static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims*
   if (!aligned16(q) || !aligned16(k)) return DBSP_ERR_INVALID_ARG;
   if (!(isfinite(score_scale))) return DBSP_ERR_INVALID_ARG;
   if (!dtype_supported(dims)) return DBSP_ERR_UNSUPPORTED;
+  if ((q_strides && !strides_ok(q_strides, dims, false)) ||
+      (k_strides && !strides_ok(k_strides, dims, false)))
+    return DBSP_ERR_INVALID_ARG;
   const int32_t nkb = nkb_of(dims);
   const int32_t nqb = nqb_of(dims);
   if (nkb > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  const dbsp::Strides qs = q_strides ? to_strides(q_strides) : contiguous(dims, dims->lq);
+  const dbsp::Strides ks = k_strides ? to_strides(k_strides) : contiguous(dims, dims->lk);
   ForcedSet fs;
   if (fs_in) {
     fs = *fs_in;
@@ -322,11 +349,14 @@ static int32_t sparse_select_impl(const void* q, const void* k, const dbsp_dims*
   const int64_t bh = (int64_t)dims->batch * dims->heads;
   uint16_t* ksplit = reinterpret_cast<uint16_t*>(ws + wl.kbar);
   const bool bf16 = dims->dtype == DBSP_BF16;
-  if (dbsp::launch_pool(k, ksplit, bh, nkb, dims->lk, dims->head_dim, bf16, s) != hipSuccess)
+  if (dbsp::launch_pool(k, ks, dims->heads, ksplit, bh, nkb, dims->lk, dims->head_dim, bf16, s) !=
+      hipSuccess)
     return DBSP_ERR_HIP;
 
   dbsp::SelectArgs a{};
   a.q = q;
+  a.qs = qs;
+  a.heads = dims->heads;
   a.ksplit = ksplit;
   a.nqb = nqb;
   a.nkb = nkb;
@@ -363,9 +393,24 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
                            int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                            float* scores_out, void* workspace, uint64_t workspace_bytes,
                            void* stream) {
-  return sparse_select_impl(q, k, dims, nullptr, text_blocks, dense_extra_blocks, mode,
-                            density_or_mass, topk_override, score_scale, row_ptr, col_idx,
-                            col_capacity, scores_out, workspace, workspace_bytes, stream);
+  return sparse_select_impl(q, k, dims, nullptr, nullptr, nullptr, text_blocks,
+                            dense_extra_blocks, mode, density_or_mass, topk_override, score_scale,
+                            row_ptr, col_idx, col_capacity, scores_out, workspace,
+                            workspace_bytes, stream);
+}
+
+int32_t dbsp_sparse_select_strided(const void* q, const dbsp_strides* q_strides, const void* k,
+                                   const dbsp_strides* k_strides, const dbsp_dims* dims,
+                                   dbsp_range text_blocks, dbsp_range dense_extra_blocks,
+                                   int32_t mode, double density_or_mass, int32_t topk_override,
+                                   float score_scale, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, float* scores_out, void* workspace,
+                                   uint64_t workspace_bytes, void* stream) {
+  if (!q_strides || !k_strides) return DBSP_ERR_INVALID_ARG;
+  return sparse_select_impl(q, k, dims, q_strides, k_strides, nullptr, text_blocks,
+                            dense_extra_blocks, mode, density_or_mass, topk_override, score_scale,
+                            row_ptr, col_idx, col_capacity, scores_out, workspace,
+                            workspace_bytes, stream);
 }
 
 int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* dims,
@@ -378,30 +423,53 @@ int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* d
   ForcedSet fs;
   const int32_t st = forced_from_list(nkb_of(dims), forced_blocks, n_forced, &fs);
   if (st != DBSP_OK) return st;
-  return sparse_select_impl(q, k, dims, &fs, dbsp_range{0, 0}, dbsp_range{0, 0}, mode,
+  return sparse_select_impl(q, k, dims, nullptr, nullptr, &fs, dbsp_range{0, 0},
+                            dbsp_range{0, 0}, mode,
                             density_or_mass, topk_override, score_scale, row_ptr, col_idx,
                             col_capacity, scores_out, workspace, workspace_bytes, stream);
 }
 
-int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
-                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
-                             float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
-                             void* stream) {
+static int32_t attn_impl(const void* q, const dbsp_strides* q_strides, const void* k,
+                         const dbsp_strides* k_strides, const void* v,
+                         const dbsp_strides* v_strides, const dbsp_dims* dims,
+                         const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                         float softmax_scale, void* o, const dbsp_strides* o_strides,
+                         int32_t o_dtype, float* lse_out, void* stream) {
   if (!shape_ok(dims) || !q || !k || !v || !row_ptr || !o) return DBSP_ERR_INVALID_ARG;
   if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
   if (o_dtype != DBSP_F32 && o_dtype != DBSP_BF16) return DBSP_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return DBSP_ERR_INVALID_ARG;
   if (!(isfinite(softmax_scale))) return DBSP_ERR_INVALID_ARG;
+  if ((q_strides && !strides_ok(q_strides, dims, false)) ||
+      (k_strides && !strides_ok(k_strides, dims, false)) ||
+      (v_strides && !strides_ok(v_strides, dims, false)))
+    return DBSP_ERR_INVALID_ARG;
+  if (o_strides) {
+    // O is written in o_dtype: rows must hold head_dim elements and stay 16-byte aligned
+    dbsp_dims od = *dims;
+    od.dtype = o_dtype;
+    if (!strides_ok(o_strides, &od, true)) return DBSP_ERR_INVALID_ARG;
+  }
   if (!attn_supported(dims)) return DBSP_ERR_UNSUPPORTED;
-  if (dims->dtype == DBSP_BF16 && nkb_of(dims) > kMaxBf16KeyBlocks)
-    return DBSP_ERR_UNSUPPORTED;
+  const dbsp::Strides ks = k_strides ? to_strides(k_strides) : contiguous(dims, dims->lk);
+  const dbsp::Strides vs = v_strides ? to_strides(v_strides) : contiguous(dims, dims->lk);
+  if (dims->dtype == DBSP_BF16) {
+    if (nkb_of(dims) > kMaxBf16KeyBlocks) return DBSP_ERR_UNSUPPORTED;
+    // a head's K and V are addressed with 32-bit byte offsets
+    const int64_t span = ((int64_t)nkb_of(dims) * DBSP_BLOCK) * 2;
+    if (span * ks.t > INT32_MAX || span * vs.t > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  }
   const float scale = softmax_scale > 0.f ? softmax_scale
                                           : (float)(1.0 / sqrt((double)dims->head_dim));
   dbsp::AttnArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
+  a.qs = q_strides ? to_strides(q_strides) : contiguous(dims, dims->lq);
+  a.ks = ks;
+  a.vs = vs;
+  a.os = o_strides ? to_strides(o_strides) : contiguous(dims, dims->lq);
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.col_capacity = col_capacity;
@@ -419,6 +487,26 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return DBSP_ERR_HIP;
   return DBSP_OK;
+}
+
+int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const dbsp_dims* dims,
+                             const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
+                             float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
+                             void* stream) {
+  return attn_impl(q, nullptr, k, nullptr, v, nullptr, dims, row_ptr, col_idx, col_capacity,
+                   softmax_scale, o, nullptr, o_dtype, lse_out, stream);
+}
+
+int32_t dbsp_sparse_attn_fwd_strided(const void* q, const dbsp_strides* q_strides, const void* k,
+                                     const dbsp_strides* k_strides, const void* v,
+                                     const dbsp_strides* v_strides, const dbsp_dims* dims,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_capacity, float softmax_scale, void* o,
+                                     const dbsp_strides* o_strides, int32_t o_dtype,
+                                     float* lse_out, void* stream) {
+  if (!q_strides || !k_strides || !v_strides || !o_strides) return DBSP_ERR_INVALID_ARG;
+  return attn_impl(q, q_strides, k, k_strides, v, v_strides, dims, row_ptr, col_idx,
+                   col_capacity, softmax_scale, o, o_strides, o_dtype, lse_out, stream);
 }
 
 int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, float softmax_scale,

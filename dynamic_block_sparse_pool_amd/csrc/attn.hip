@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
     const uint16_t* __restrict__ vg, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int64_t col_capacity, int nqb, int nkb, int64_t lq,
-    int64_t lk, float scale_log2, void* __restrict__ o, int o_bf16, float* __restrict__ lse) {
+    int64_t lk, int heads, Strides qs, Strides ks, Strides vs, Strides os, float scale_log2,
+    void* __restrict__ o, int o_bf16, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kBlock * 128];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kBlock * 128];
   __shared__ int list[kListCap];
@@ -156,19 +157,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int klast = (int)(lk - (int64_t)(nkb - 1) * kBlock);
   const int tail = kTail ? nkb - 1 : -1;
 
-  // K and V of this (batch, head): lk x 128 bf16 each; the DMA reads whole blocks only
-  const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kg + bh * lk * 128, (uint32_t)(lk * 256));
-  const __amdgpu_buffer_rsrc_t vbuf = raw_buffer(vg + bh * lk * 128, (uint32_t)(lk * 256));
-  const DmaOffsets dmo = dma_offsets(lane);
-  constexpr int kTileBytes = kBlock * 128 * 2;
+  // K and V of this (batch, head): lk rows of 128 bf16, rbk / rbv bytes apart (256 when
+  // contiguous); the DMA reads whole blocks only, within (lk - 1) rows + 256 bytes
+  const int rbk = (int)(ks.t * 2), rbv = (int)(vs.t * 2);
+  const uint16_t* kh = kg + token_offset(ks, bh, heads, 0);
+  const uint16_t* vh = vg + token_offset(vs, bh, heads, 0);
+  const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kh, (uint32_t)((lk - 1) * rbk + 256));
+  const __amdgpu_buffer_rsrc_t vbuf = raw_buffer(vh, (uint32_t)((lk - 1) * rbv + 256));
+  const DmaOffsets dmo = dma_offsets(lane, rbk, rbv);
+  const int kTileK = kBlock * rbk, kTileV = kBlock * rbv;  // bytes between key blocks
 
   // Q^T as the B operand of S^T = K Q^T: lane (h, l32) holds query 32 w + l32, dims 16 s + 8 h .. +7
   const int64_t qi = (int64_t)qb * kBlock + 32 * w + l32;  // query within the (batch, head)
   const bool q_valid = qi < lq;
-  const int64_t qtok = bh * lq + qi;
+  const int64_t qtok = bh * lq + qi;                       // lse index (contiguous)
   bf16x8 qf[8];
   {
-    const uint16_t* qr = qg + (q_valid ? qtok : bh * lq) * 128 + 8 * h;
+    const uint16_t* qr = qg + token_offset(qs, bh, heads, q_valid ? qi : 0) + 8 * h;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     if (n == 0) continue;
     {
       const int cb = __builtin_amdgcn_readfirstlane(list[0]);
-      tile_dma<false>(kbuf, cb * kTileBytes, k_lds, w, dmo);
-      tile_dma<true>(vbuf, cb * kTileBytes, v_lds, w, dmo);
+      tile_dma<false>(kbuf, cb * kTileK, k_lds, w, dmo, rbk);
+      tile_dma<true>(vbuf, cb * kTileV, v_lds, w, dmo, rbv);
     }
     for (int i = 0; i < n; ++i) {
       const bool more = i + 1 < n;
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       const int cb_next = __builtin_amdgcn_readfirstlane(list[more ? i + 1 : i]);
       wait_lgkmcnt0();
       wg_barrier();  // every wave is done reading K(i)
-      tile_dma<false>(kbuf, cb_next * kTileBytes, k_lds, w, dmo);
+      tile_dma<false>(kbuf, cb_next * kTileK, k_lds, w, dmo, rbk);
 
       bf16x8 pf[8];
       softmax_tile(sacc, scale_log2, m_run, l_run, oacc, pf);
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       }
       wait_lgkmcnt0();
       wg_barrier();  // every wave is done reading V(i)
-      tile_dma<true>(vbuf, cb_next * kTileBytes, v_lds, w, dmo);
+      tile_dma<true>(vbuf, cb_next * kTileV, v_lds, w, dmo, rbv);
     }
     wait_vmcnt<0>();
   }
@@ -265,13 +270,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     wg_barrier();  // every wave's DMAs have landed and every wave is done with the tiles
-    const int64_t tok = bh * lk + (int64_t)tail * kBlock;
+    const int64_t tok = (int64_t)tail * kBlock;
     // opaque copy of the thread index: keeps the copy's address arithmetic inside this block
     // (hoisted above the main loop it would hold registers through it)
     int t_opaque = tid;
     asm volatile("" : "+v"(t_opaque));
-    tile_load_partial<false>(kg + tok * 128, klast, k_lds, t_opaque);
-    tile_load_partial<true>(vg + tok * 128, klast, v_lds, t_opaque);
+    tile_load_partial<false>(kh + tok * ks.t, klast, k_lds, t_opaque, ks.t);
+    tile_load_partial<true>(vh + tok * vs.t, klast, v_lds, t_opaque, vs.t);
     __syncthreads();
     // tile bases offset by an opaque zero, so that the reads below do not share (and keep live
     // through the main loop) the loop's precomputed LDS addresses
@@ -298,8 +303,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (!q_valid) return;
+  const int64_t otok = token_offset(os, bh, heads, qi);
   if (o_bf16) {
-    uint16_t* orow = static_cast<uint16_t*>(o) + qtok * 128;
+    uint16_t* orow = static_cast<uint16_t*>(o) + otok;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + n0) = pk;
       }
   } else {
-    float* orow = static_cast<float*>(o) + qtok * 128;
+    float* orow = static_cast<float*>(o) + otok;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -339,10 +345,10 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   const int t = threadIdx.x;
   const int64_t qi = (int64_t)qb * kBlock + t;
   const bool q_valid = qi < a.lq;
-  const int64_t qtok = bh * a.lq + (q_valid ? qi : 0);
-  const float* qp = static_cast<const float*>(a.q) + qtok * D;
-  const float* kp = static_cast<const float*>(a.k) + bh * a.lk * D;
-  const float* vp = static_cast<const float*>(a.v) + bh * a.lk * D;
+  const int64_t qtok = bh * a.lq + (q_valid ? qi : 0);  // lse index (contiguous)
+  const float* qp = static_cast<const float*>(a.q) + token_offset(a.qs, bh, a.heads, q_valid ? qi : 0);
+  const float* kp = static_cast<const float*>(a.k) + token_offset(a.ks, bh, a.heads, 0);
+  const float* vp = static_cast<const float*>(a.v) + token_offset(a.vs, bh, a.heads, 0);
 
   float qv[D];
 #pragma unroll
@@ -362,12 +368,13 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
     // skipped below
     const int valid = (int)(a.lk - (int64_t)cb * kBlock < kBlock ? a.lk - (int64_t)cb * kBlock
                                                                  : kBlock);
-    const float* kb = kp + (int64_t)cb * kBlock * D;
-    const float* vb = vp + (int64_t)cb * kBlock * D;
+    const float* kb = kp + (int64_t)cb * kBlock * a.ks.t;
+    const float* vb = vp + (int64_t)cb * kBlock * a.vs.t;
     for (int i = t; i < kBlock * D; i += 128) {
-      const bool in = i < valid * D;
-      (&k_lds[0][0])[i] = in ? kb[i] : 0.f;
-      (&v_lds[0][0])[i] = in ? vb[i] : 0.f;
+      const int r = i / D, col = i - (i / D) * D;
+      const bool in = r < valid;
+      (&k_lds[0][0])[i] = in ? kb[r * a.ks.t + col] : 0.f;
+      (&v_lds[0][0])[i] = in ? vb[r * a.vs.t + col] : 0.f;
     }
     __syncthreads();
     for (int j0 = 0; j0 < valid; j0 += 32) {
@@ -399,12 +406,13 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   }
   if (!q_valid) return;
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  const int64_t otok = token_offset(a.os, bh, a.heads, qi);
   if (a.o_bf16) {
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + qtok * D;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + otok;
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = (uint16_t)f32_to_bf16_bits(acc[d] * inv);
   } else {
-    float* orow = static_cast<float*>(a.o) + qtok * D;
+    float* orow = static_cast<float*>(a.o) + otok;
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
   }
@@ -418,7 +426,7 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t s
                                                                                   stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), a.row_ptr, a.col_idx, a.col_capacity, a.nqb, a.nkb,
-        a.lq, a.lk, a.scale_log2, a.o, a.o_bf16, a.lse);
+        a.lq, a.lk, a.heads, a.qs, a.ks, a.vs, a.os, a.scale_log2, a.o, a.o_bf16, a.lse);
   else if (!bf16 && head_dim == 64)
     attn_fwd_f32_kernel<64><<<grid, 128, 0, stream>>>(a);
   else if (!bf16 && head_dim == 128)

@@ -40,7 +40,7 @@ __device__ __forceinline__ const uint16_t* energy_step_begin(int g, int n, uint1
   wg_barrier();
   const int gn = g + 1 < 2 * n ? g + 1 : g;
   const int cn = gn < n ? gn : gn - n;
-  tile_dma<false>(kbuf, cn * kTileBytes, k_lds + ((g + 1) & 1) * (kBlock * 128), w, dmo);
+  tile_dma<false>(kbuf, cn * kTileBytes, k_lds + ((g + 1) & 1) * (kBlock * 128), w, dmo, 256);
   return k_lds + (g & 1) * (kBlock * 128);
 }
 
@@ -51,7 +51,7 @@ __device__ __forceinline__ const uint16_t* energy_tail_tile(const uint16_t* ktai
   wait_lgkmcnt0();
   wg_barrier();  // every wave is done with buffer `buf`
   uint16_t* kt = k_lds + buf * (kBlock * 128);
-  tile_load_partial<false>(ktail, klast, kt, tid);
+  tile_load_partial<false>(ktail, klast, kt, tid, 128);
   __syncthreads();
   return kt;
 }
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void block_energy_bf16_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kg + bh * lk * 128, (uint32_t)(lk * 256));
-  const DmaOffsets dmo = dma_offsets(lane);
+  const DmaOffsets dmo = dma_offsets(lane, 256, 256);
   // whole key blocks go through the DMA pipeline; a partial last one is handled apart
   const int klast = (int)(lk - (int64_t)(nkb - 1) * kBlock);
   const bool has_tail = klast < kBlock;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void block_energy_bf16_kernel(
     }
   }
 
-  if (nfull > 0) tile_dma<false>(kbuf, 0, k_lds, w, dmo);
+  if (nfull > 0) tile_dma<false>(kbuf, 0, k_lds, w, dmo, 256);
 
   // sweep 1: log-sum-exp per query (lanes l32 and l32 + 32 hold halves of the same query)
   float m_run = -INFINITY, l_run = 0.f;

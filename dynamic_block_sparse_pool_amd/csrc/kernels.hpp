@@ -6,11 +6,26 @@
 
 namespace dbsp {
 
+// Element strides of a [batch, heads, tokens, head_dim] view (the innermost dimension is
+// contiguous). Contiguous tensors have {heads * L * d, L * d, d}; a [batch, L, heads, d] tensor
+// seen head-major has {L * heads * d, d, heads * d}.
+struct Strides {
+  int64_t b, h, t;
+};
+
+// Element offset of token t of (batch, head) pair bh = b * heads + h.
+__host__ __device__ __forceinline__ int64_t token_offset(const Strides& s, int64_t bh, int heads,
+                                                         int64_t t) {
+  return (bh / heads) * s.b + (bh % heads) * s.h + t * s.t;
+}
+
 // Largest forced set passed as a bitmask in the kernel arguments: one bit per key block.
 constexpr int kMaxForcedWords = 32;  // 2048 key blocks
 
 struct SelectArgs {
-  const void* q;           // queries [BH, nqb * 128, D] (bf16 or fp32), pooled in the kernel
+  const void* q;           // queries (bf16 or fp32), pooled in the kernel
+  Strides qs;              // ... laid out with these strides
+  int heads;               // H, to split the (batch, head) index
   const uint16_t* ksplit;  // pooled keys as bf16 hi | lo in MFMA tile order (workspace):
                            // [BH][ceil(nkb / 16)][D / 32][hi | lo][64 lanes][8]
   int nqb, nkb;
@@ -39,6 +54,7 @@ struct AttnArgs {
   const void* q;
   const void* k;
   const void* v;
+  Strides qs, ks, vs, os;  // element strides of Q, K, V and O
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int64_t col_capacity;
@@ -90,8 +106,8 @@ struct AnchorArgs {
 };
 
 // Pooled keys of every (batch, head): bh heads of lk tokens each, nkb = ceil(lk / 128) blocks.
-hipError_t launch_pool(const void* k, uint16_t* ksplit, int64_t bh, int nkb, int64_t lk,
-                       int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_pool(const void* k, const Strides& ks, int heads, uint16_t* ksplit, int64_t bh,
+                       int nkb, int64_t lk, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int64_t bh, int head_dim, bool bf16,
                          hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream);

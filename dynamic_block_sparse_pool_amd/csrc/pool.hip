@@ -2,8 +2,8 @@
 // method overview, block partition bullet: the vectors inside each 128-token block are averaged;
 // a partial last block, when lk is not a multiple of 128, averages the tokens it holds).
 //
-// One workgroup per key block of a (batch, head): up to 128 consecutive rows of head_dim
-// elements, contiguous in memory. Each of the 256 threads owns one 16-byte column chunk of
+// One workgroup per key block of a (batch, head): up to 128 consecutive tokens of head_dim
+// contiguous elements each, the tokens a fixed stride apart. Each of the 256 threads owns one 16-byte column chunk of
 // 128 / (256 / chunks) rows, issues all of its loads before any arithmetic (rows past the end of
 // a partial block are not read), sums in fp32, and the partial column sums meet in LDS. Output
 // per block: the fp32 mean m split as hi = bf16(m) and lo = bf16(m - hi), in the tiled operand
@@ -26,9 +26,9 @@ __device__ __forceinline__ int64_t ktile_offset(int64_t bh, int n, int ntiles, i
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ k,
-                                                          uint16_t* __restrict__ kbar, int nkb,
-                                                          int64_t lk) {
+__global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ k, Strides ks,
+                                                          int heads, uint16_t* __restrict__ kbar,
+                                                          int nkb, int64_t lk) {
   constexpr int kVec = 16 / (int)sizeof(T);       // elements per 16-byte chunk
   constexpr int kChunks = D / kVec;               // chunks per row
   constexpr int kRowsPerPass = 256 / kChunks;     // rows covered by one pass of the workgroup
@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
   const int n = (int)(g - bh * nkb);
   const int64_t first = (int64_t)n * kBlock;
   const int valid = (int)(lk - first < kBlock ? lk - first : kBlock);  // 1 .. 128
-  const T* src = k + (bh * lk + first) * D;
+  const T* src = k + token_offset(ks, bh, heads, first);
+  const int64_t st = ks.t;  // elements between consecutive tokens
   const int t = threadIdx.x;
   const int chunk = t % kChunks;
   const int row0 = t / kChunks;
@@ -52,13 +53,13 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
       raw[p] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(src + (int64_t)(row0 + p * kRowsPerPass) * D) + chunk);
+          reinterpret_cast<const u32x4*>(src + (int64_t)(row0 + p * kRowsPerPass) * st) + chunk);
   } else {
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       const int row = row0 + p * kRowsPerPass;
       raw[p] = row < valid ? __builtin_nontemporal_load(
-                                 reinterpret_cast<const u32x4*>(src + (int64_t)row * D) + chunk)
+                                 reinterpret_cast<const u32x4*>(src + (int64_t)row * st) + chunk)
                            : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -95,19 +96,21 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T* __restrict__ 
   }
 }
 
-hipError_t launch_pool(const void* k, uint16_t* kbar, int64_t bh, int nkb, int64_t lk,
-                       int head_dim, bool bf16, hipStream_t stream) {
+hipError_t launch_pool(const void* k, const Strides& ks, int heads, uint16_t* kbar, int64_t bh,
+                       int nkb, int64_t lk, int head_dim, bool bf16, hipStream_t stream) {
   dim3 grid((unsigned)(bh * nkb)), block(256);
   if (bf16 && head_dim == 128)
-    pool_blocks_kernel<uint16_t, 128><<<grid, block, 0, stream>>>((const uint16_t*)k, kbar, nkb,
-                                                                   lk);
+    pool_blocks_kernel<uint16_t, 128><<<grid, block, 0, stream>>>((const uint16_t*)k, ks, heads,
+                                                                   kbar, nkb, lk);
   else if (bf16 && head_dim == 64)
-    pool_blocks_kernel<uint16_t, 64><<<grid, block, 0, stream>>>((const uint16_t*)k, kbar, nkb,
-                                                                  lk);
+    pool_blocks_kernel<uint16_t, 64><<<grid, block, 0, stream>>>((const uint16_t*)k, ks, heads,
+                                                                  kbar, nkb, lk);
   else if (!bf16 && head_dim == 64)
-    pool_blocks_kernel<float, 64><<<grid, block, 0, stream>>>((const float*)k, kbar, nkb, lk);
+    pool_blocks_kernel<float, 64><<<grid, block, 0, stream>>>((const float*)k, ks, heads, kbar,
+                                                               nkb, lk);
   else if (!bf16 && head_dim == 128)
-    pool_blocks_kernel<float, 128><<<grid, block, 0, stream>>>((const float*)k, kbar, nkb, lk);
+    pool_blocks_kernel<float, 128><<<grid, block, 0, stream>>>((const float*)k, ks, heads, kbar,
+                                                                nkb, lk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

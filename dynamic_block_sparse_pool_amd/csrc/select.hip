@@ -97,10 +97,11 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
   const bool live0 = row0 + rr0 < a.nqb, live1 = row0 + rr0 + 1 < a.nqb;
   if (!live0) return;
   const int64_t first0 = (int64_t)(row0 + rr0) * kBlock;  // first token of block rr0
-  const T* src0 = static_cast<const T*>(a.q) + ((int64_t)bh * a.lq + first0) * D +
-                  (int64_t)r0 * D + chunk * kVec;
+  const int64_t st = a.qs.t;                                // elements between tokens
+  const T* src0 = static_cast<const T*>(a.q) + token_offset(a.qs, bh, a.heads, first0) +
+                  (int64_t)r0 * st + chunk * kVec;
   // the second block is only read when it exists; otherwise the first is read twice
-  const T* src1 = live1 ? src0 + (int64_t)kBlock * D : src0;
+  const T* src1 = live1 ? src0 + (int64_t)kBlock * st : src0;
   // tokens held by each block (a partial last block holds fewer than 128; rows past it are
   // not read)
   const int valid0 = (int)(a.lq - first0 < kBlock ? a.lq - first0 : kBlock);
@@ -127,7 +128,7 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
       u32x4 raw0[kBatch], raw1[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
+        const int64_t off = (int64_t)(b + i) * kRowsPerLoad * st;
         raw0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off));
         raw1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src1 + off));
       }
@@ -144,7 +145,7 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int row = (b + i) * kRowsPerLoad + r0;
-        const int64_t off = (int64_t)(b + i) * kRowsPerLoad * D;
+        const int64_t off = (int64_t)(b + i) * kRowsPerLoad * st;
         raw0[i] = row < valid0
                       ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src0 + off))
                       : u32x4{0u, 0u, 0u, 0u};

@@ -35,20 +35,21 @@ __device__ __forceinline__ void wg_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Per-lane byte offsets (inside a 4-row, 1 KiB slab) of the global source of a tile DMA. For
-// slab i (rows 4 i .. 4 i + 3 of the wave's 32) the swizzle depends on the row only modulo 16
-// (K) or 4 (V), so K needs four offsets (i mod 4) and V one.
+// Per-lane byte offsets (inside a 4-row slab) of the global source of a tile DMA, for K rows
+// rbk bytes apart and V rows rbv bytes apart (256 for contiguous bf16 x 128 tensors). For slab i
+// (rows 4 i .. 4 i + 3 of the wave's 32) the swizzle depends on the row only modulo 16 (K) or
+// 4 (V), so K needs four offsets (i mod 4) and V one.
 struct DmaOffsets {
   uint32_t k[4];
   uint32_t v;
 };
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane, int rbk, int rbv) {
   DmaOffsets d;
   const int r = lane >> 4, pc = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d.k[i] = (uint32_t)(r * 256 + k_swz(4 * i + r, pc) * 16);
-  d.v = (uint32_t)(r * 256 + v_swz(r, pc) * 16);
+  for (int i = 0; i < 4; ++i) d.k[i] = (uint32_t)(r * rbk + k_swz(4 * i + r, pc) * 16);
+  d.v = (uint32_t)(r * rbv + v_swz(r, pc) * 16);
   return d;
 }
 
@@ -59,20 +60,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, u
                                            0x00020000);
 }
 
-// Issue the DMA of one 128 x 128 bf16 tile (32 KiB at byte `tile_off` of the head's K or V,
-// wave-uniform) into LDS: wave w copies rows 32 w .. 32 w + 31, one 4-row slab (1 KiB) per
-// instruction, lane l landing at byte 16 l of the slab, so the swizzle is applied on the global
-// side. The buffer form takes the tile offset in a scalar register and the lane offset in a
-// 32-bit vector register, so the addressing costs no vector instructions.
+// Issue the DMA of one 128 x 128 bf16 tile (128 rows `rb` bytes apart, starting at byte
+// `tile_off` of the head's K or V, wave-uniform) into LDS: wave w copies rows 32 w .. 32 w + 31,
+// one 4-row slab (1 KiB of LDS) per instruction, lane l landing at byte 16 l of the slab, so the
+// swizzle is applied on the global side. The buffer form takes the row offset in a scalar
+// register and the lane offset in a 32-bit vector register, so the addressing costs no vector
+// instructions.
 template <bool kIsV>
 __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t src, int tile_off, uint16_t* lds,
-                                         int w, const DmaOffsets& d) {
-  const int wave_off = tile_off + w * (32 * 256);
+                                         int w, const DmaOffsets& d, int rb) {
+  const int wave_off = tile_off + w * 32 * rb;
   uint16_t* wave_dst = lds + w * (32 * 128);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)(wave_dst + 4 * i * 128), 16,
-                                             kIsV ? d.v : d.k[i & 3], wave_off + 4 * i * 256, 0,
+                                             kIsV ? d.v : d.k[i & 3], wave_off + 4 * i * rb, 0,
                                              0);
 }
 
@@ -100,18 +102,19 @@ __device__ __forceinline__ int sacc_key(int jt, int r, int h) {
   return 32 * jt + 8 * (r >> 2) + 4 * h + (r & 3);
 }
 
-// Plain (not DMA) copy of a partial tile: rows [0, valid) of `src` (128 bf16 per row) into the
-// swizzled LDS layout, rows [valid, 128) zero-filled. All 256 threads of the workgroup take
-// part; the caller synchronises before and after.
+// Plain (not DMA) copy of a partial tile: rows [0, valid) of `src` (128 bf16 per row, rows
+// `stride` elements apart) into the swizzled LDS layout, rows [valid, 128) zero-filled. All 256
+// threads of the workgroup take part; the caller synchronises before and after.
 template <bool kIsV>
 __device__ __forceinline__ void tile_load_partial(const uint16_t* src, int valid, uint16_t* lds,
-                                                  int tid) {
+                                                  int tid, int64_t stride) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = tid + 256 * i;  // 16-byte chunk of the tile
     const int row = q >> 4, lc = q & 15;
-    const u32x4 v = row < valid ? *reinterpret_cast<const u32x4*>(src + row * 128 + lc * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 v = row < valid
+                        ? *reinterpret_cast<const u32x4*>(src + row * stride + lc * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
     const int pc = kIsV ? v_swz(row, lc) : k_swz(row, lc);
     *reinterpret_cast<u32x4*>(lds + row * 128 + pc * 8) = v;
   }

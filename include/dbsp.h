@@ -34,7 +34,8 @@
  *
  * Conventions shared by every call
  *   Layout     Q is [batch, heads, lq, head_dim]; K and V are [batch, heads, lk, head_dim];
- *              all contiguous row-major and 16-byte aligned. lq, lk >= 1.
+ *              all contiguous row-major and 16-byte aligned (the *_strided calls take other
+ *              layouts, e.g. [batch, L, heads, head_dim]). lq, lk >= 1.
  *              Block i of a sequence is tokens [128 i, min(128 i + 128, L)): a length that is
  *              not a multiple of 128 ends in a partial block, which pools to the mean of the
  *              tokens it holds and contributes only those tokens to attention and energies
@@ -96,6 +97,16 @@ typedef struct dbsp_dims {
   int32_t head_dim;
   int32_t dtype;
 } dbsp_dims;
+
+/* Element strides of a [batch, heads, tokens, head_dim] view whose head_dim elements are
+ * contiguous: token (b, h, t) starts at element b * batch + h * head + t * token. Contiguous
+ * tensors are {heads * L * head_dim, L * head_dim, head_dim}; a [batch, L, heads, head_dim]
+ * tensor is {L * heads * head_dim, head_dim, heads * head_dim}. Used by the *_strided calls. */
+typedef struct {
+  int64_t batch;
+  int64_t head;
+  int64_t token;
+} dbsp_strides;
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int32_t dbsp_version(void);
@@ -174,6 +185,21 @@ int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* d
                                 float* scores_out, void* workspace, uint64_t workspace_bytes,
                                 void* stream);
 
+/*
+ * dbsp_sparse_select on strided Q and K views (dbsp_strides, in elements of the input dtype):
+ * for example [batch, L, heads, head_dim] tensors, or K shared by all heads of a batch entry
+ * (head stride 0). Strides must be non-negative with every token row 16-byte aligned.
+ * Everything else is as dbsp_sparse_select. Errors: DBSP_ERR_INVALID_ARG for NULL or bad
+ * strides; otherwise as dbsp_sparse_select.
+ */
+int32_t dbsp_sparse_select_strided(const void* q, const dbsp_strides* q_strides, const void* k,
+                                   const dbsp_strides* k_strides, const dbsp_dims* dims,
+                                   dbsp_range text_blocks, dbsp_range dense_extra_blocks,
+                                   int32_t mode, double density_or_mass, int32_t topk_override,
+                                   float score_scale, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, float* scores_out, void* workspace,
+                                   uint64_t workspace_bytes, void* stream);
+
 /* dbsp_select_nnz_bound for a forced list (host memory, as dbsp_sparse_select_list). */
 int32_t dbsp_select_nnz_bound_list(const dbsp_dims* dims, int32_t mode, double density_or_mass,
                                    const int32_t* forced_blocks, int32_t n_forced,
@@ -202,6 +228,23 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
                              const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
                              float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
                              void* stream);
+
+/*
+ * dbsp_sparse_attn_fwd on strided Q, K, V and O views (dbsp_strides in elements: Q, K, V in the
+ * input dtype, O in o_dtype). Strides must be non-negative with every token row 16-byte
+ * aligned; O's token stride must be at least head_dim (rows of different heads or batch
+ * entries must not overlap either; that is not checked). lse_out stays contiguous
+ * [batch, heads, lq]. bf16 inputs also need (lk rounded up to 128) * token stride * 2 bytes
+ * below 2^31 for K and V. Errors as dbsp_sparse_attn_fwd, plus DBSP_ERR_INVALID_ARG for NULL
+ * or bad strides.
+ */
+int32_t dbsp_sparse_attn_fwd_strided(const void* q, const dbsp_strides* q_strides, const void* k,
+                                     const dbsp_strides* k_strides, const void* v,
+                                     const dbsp_strides* v_strides, const dbsp_dims* dims,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_capacity, float softmax_scale, void* o,
+                                     const dbsp_strides* o_strides, int32_t o_dtype,
+                                     float* lse_out, void* stream);
 
 /*
  * Token-level block energy ([CalibAtt] key design 1, Eq. (5)).

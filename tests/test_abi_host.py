@@ -316,3 +316,33 @@ def test_skiplist_calls_reject_bad_arguments(lib):
         assert dec(**kw) == E.DBSP_ERR_INVALID_ARG, kw
     assert dec(cap=31) == E.DBSP_ERR_CAPACITY             # 4 rows x 8 blocks
     assert dec(ws=ctypes.c_void_p((1 << 20) + 8)) == E.DBSP_ERR_WORKSPACE
+
+
+def test_strided_calls_reject_bad_strides(lib):
+    E = _abi
+    dims = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_BF16)
+    good = _abi.Strides(2 * 256 * 128, 256 * 128, 128)
+
+    def attn(qs=good, ks=good, vs=good, os_=_abi.Strides(2 * 256 * 128, 256 * 128, 128),
+             odt=E.DBSP_F32):
+        args = [ctypes.byref(x) if x is not None else None for x in (qs, ks, vs, os_)]
+        return lib.dbsp_sparse_attn_fwd_strided(FAKE, args[0], FAKE, args[1], FAKE, args[2],
+                                                ctypes.byref(dims), FAKE, FAKE, 16, 0.0, FAKE,
+                                                args[3], odt, None, None)
+
+    for kw in ({"qs": None}, {"os_": None},
+               {"ks": _abi.Strides(-1, 128, 128)},              # negative
+               {"qs": _abi.Strides(0, 0, 100)},                 # rows not 16-byte aligned
+               {"os_": _abi.Strides(0, 0, 64)}):                # output rows overlap
+        assert attn(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+
+    def sel(qs=good, ks=good):
+        args = [ctypes.byref(x) if x is not None else None for x in (qs, ks)]
+        return lib.dbsp_sparse_select_strided(FAKE, args[0], FAKE, args[1], ctypes.byref(dims),
+                                              _abi.Range(0, 1), _abi.Range(0, 0), E.DBSP_TOPK,
+                                              0.5, -1, 0.0, FAKE, FAKE, 1 << 40, None, None, 0,
+                                              None)
+
+    assert sel(ks=None) == E.DBSP_ERR_INVALID_ARG
+    assert sel(qs=_abi.Strides(0, 3, 128)) == E.DBSP_ERR_INVALID_ARG
+    assert sel() == E.DBSP_ERR_WORKSPACE      # valid strides reach the workspace check
