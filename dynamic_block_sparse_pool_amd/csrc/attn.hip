@@ -132,8 +132,10 @@ __device__ __forceinline__ void pv_tile(const uint16_t* v_lds, const bf16x8 (&pf
 // the DMA pipeline and processed once at the end from plain, bounds-checked loads with its
 // missing keys masked (kTail variant only: the extra code raises register pressure in the main
 // loop, so whole-block shapes run the variant without it); queries past lq are computed on
-// zeros and not stored.
-template <bool kTail>
+// zeros and not stored. kDenseRows: K and V rows are 128 contiguous bf16 (256 bytes apart, the
+// common layout), which turns the DMA's row offsets into constants the compiler keeps in
+// precomputed scalar registers; other strides take the variant with run-time row offsets.
+template <bool kTail, bool kDenseRows>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
     const uint16_t* __restrict__ vg, const int32_t* __restrict__ row_ptr,
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 
   // K and V of this (batch, head): lk rows of 128 bf16, rbk / rbv bytes apart (256 when
   // contiguous); the DMA reads whole blocks only, within (lk - 1) rows + 256 bytes
-  const int rbk = (int)(ks.t * 2), rbv = (int)(vs.t * 2);
+  const int rbk = kDenseRows ? 256 : (int)(ks.t * 2), rbv = kDenseRows ? 256 : (int)(vs.t * 2);
   const uint16_t* kh = kg + token_offset(ks, bh, heads, 0);
   const uint16_t* vh = vg + token_offset(vs, bh, heads, 0);
   const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kh, (uint32_t)((lk - 1) * rbk + 256));
@@ -421,13 +423,17 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   dim3 grid((unsigned)a.rows);
-  if (bf16 && head_dim == 128)
-    (a.lk % kBlock ? attn_fwd_bf16_kernel<true> : attn_fwd_bf16_kernel<false>)<<<grid, 256, 0,
-                                                                                  stream>>>(
+  if (bf16 && head_dim == 128) {
+    const bool tail = a.lk % kBlock != 0, dense = a.ks.t == 128 && a.vs.t == 128;
+    auto* kern = tail ? (dense ? attn_fwd_bf16_kernel<true, true>
+                               : attn_fwd_bf16_kernel<true, false>)
+                      : (dense ? attn_fwd_bf16_kernel<false, true>
+                               : attn_fwd_bf16_kernel<false, false>);
+    kern<<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), a.row_ptr, a.col_idx, a.col_capacity, a.nqb, a.nkb,
         a.lq, a.lk, a.heads, a.qs, a.ks, a.vs, a.os, a.scale_log2, a.o, a.o_bf16, a.lse);
-  else if (!bf16 && head_dim == 64)
+  } else if (!bf16 && head_dim == 64)
     attn_fwd_f32_kernel<64><<<grid, 128, 0, stream>>>(a);
   else if (!bf16 && head_dim == 128)
     attn_fwd_f32_kernel<128><<<grid, 128, 0, stream>>>(a);
