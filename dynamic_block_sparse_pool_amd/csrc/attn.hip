@@ -8,11 +8,16 @@
 // attn_fwd_bf16_kernel (bf16, head_dim 128): one workgroup of 4 waves per CSR row (one query
 // block of 128 tokens); wave w owns queries [32 w, 32 w + 32). Per kept key block:
 //   * K [128 x 128] and V [128 x 128] are copied to LDS (XOR-swizzled against bank conflicts);
-//   * S^T = K Q^T on 32x32x16 bf16 MFMAs: Q^T is the B operand, held in registers for the
-//     whole row; the result leaves every lane with one query column and 64 key rows, so the
-//     row max needs one cross-half exchange;
+//   * the block is processed in four sub-tiles of 32 keys; S^T = K Q^T on 32x32x16 bf16 MFMAs
+//     (Q^T is the B operand, held in registers for the whole row) leaves every lane with one
+//     query column and 16 keys of the sub-tile;
+//   * the sub-tiles are software-pipelined: the softmax of sub-tile u runs next to the QK
+//     MFMAs of u + 1 and the PV MFMAs of u - 1, so the vector ALU and the matrix cores of a
+//     wave overlap;
 //   * an fp32 online softmax in the exp2 domain (the log2(e) factor folded into the scale)
-//     whose exponent reference is raised lazily, only when a block exceeds it by 2^8;
+//     whose reference is raised lazily: probabilities are formed against the current reference
+//     first, and only a sub-tile whose partial row sums break a bound takes its exact maximum
+//     and rescales O and l, so the row maximum is not computed in the common case;
 //   * O^T += V^T P^T: the probabilities go straight from the S^T accumulators (as bf16) into
 //     the B operand, and V^T comes from LDS through ds_read_tr16_b64, which transposes 4x16-bit
 //     groups across each 16-lane block on the read (the K-index order is matched to the
@@ -28,7 +33,6 @@
 namespace dbsp {
 
 constexpr int kListCap = 2048;  // kept-block indices staged in LDS per window
-constexpr float kRescaleSlack = 8.0f;  // lazy online-softmax rescale threshold, log2 units
 
 // Copy the in-range entries of col_idx[*pos, end) into list in their original order, 256
 // entries per pass (wave w takes the w-th 64), stopping before a pass that could overflow
@@ -64,66 +68,135 @@ __device__ __forceinline__ int stage_list(const int32_t* __restrict__ col_idx, i
   return total;
 }
 
-// Online softmax of one key tile for the lane's query column (lanes l32 and l32 + 32 share it),
-// exp2 domain. The exponent reference m_run is raised only when this tile's maximum exceeds it
-// by more than kRescaleSlack (log2 units), so probabilities stay below 2^kRescaleSlack and the
-// rescale of O and l is skipped for most tiles. Softmax is invariant to the reference, and l and
-// O stay consistent with the same m_run, so only rounding differs. Produces the probabilities
-// as bf16 B operands of the P V product (pf[s] = keys 16 s .. 16 s + 15 in accumulator order).
-__device__ __forceinline__ void softmax_tile(const f32x16 (&sacc)[4], float scale_log2,
-                                             float& m_run, float& l_run, f32x16 (&oacc)[4],
-                                             bf16x8 (&pf)[8]) {
-  float mx = -INFINITY;
+// Work unit of the bf16 kernel: a sub-tile of 32 keys x the wave's 32 queries. In the
+// accumulator order of S^T, register r of lane half h holds key sacc_key(jt, r, h) of the block
+// for sub-tile jt; the P operand of 16-key step j of the sub-tile takes registers 8 j .. 8 j + 7,
+// and V^T is read in the same order.
+
+// Per-lane byte offsets of a wave's LDS reads within a tile. The XOR swizzles make the offset
+// of each 16-byte K chunk step (and of each V column tile) depend on the lane, so those are
+// held in registers; rows further down (other sub-tiles, steps and halves) differ by constants
+// and go into the instructions' offset fields.
+struct LdsOff {
+  int k[8];  // K row l32 (sub-tile 0), chunk step sd
+  int v[4];  // V^T rows 4 h + tr_row (sub-tile 0, step 0, low half), column tile nt
+};
+
+__device__ __forceinline__ LdsOff lds_offsets(int l32, int h, int tr_row, int tr_col) {
+  LdsOff o;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int sd = 0; sd < 8; ++sd) o.k[sd] = 2 * (l32 * 128 + k_swz(l32, 2 * sd + h) * 8);
+  const int jb = 4 * h + tr_row;  // jb & 3 == tr_row for every row read below
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (__ballot(mx * scale_log2 > m_run + kRescaleSlack) != 0ull) {
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = 32 * nt + tr_col;
+    o.v[nt] = 2 * (jb * 128 + v_swz(jb, col >> 3) * 8 + (col & 7));
+  }
+  return o;
+}
+
+// A copy of the offsets that the compiler cannot see through, taken once per block: the
+// tile-base additions then stay next to their reads instead of being hoisted out of the loop
+// for every sub-tile, where they would hold registers for the whole row.
+__device__ __forceinline__ LdsOff lds_opaque(const LdsOff& in) {
+  LdsOff o = in;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(o.k[i]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(o.v[i]));
+  return o;
+}
+
+// S^T of sub-tile jt of the K tile at kt x the wave's queries: 32 keys x 32 queries.
+__device__ __forceinline__ void qk_sub(const uint16_t* kt, const LdsOff& lo,
+                                       const bf16x8 (&qf)[8], int jt, f32x16& s) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int sd = 0; sd < 8; ++sd) {
+    // sub-tile jt: 32 rows (8 KiB) further; k_swz depends on the row only modulo 16
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+        reinterpret_cast<const char*>(kt) + lo.k[sd] + jt * 8192);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[sd], s, 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T over sub-tile jt of the V tile at vt (V^T through transposing LDS reads of the
+// swizzled tile).
+__device__ __forceinline__ void pv_sub(const uint16_t* vt, const LdsOff& lo,
+                                       const bf16x8 (&pf)[2], int jt, f32x16 (&oacc)[4]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    // rows 32 jt + 16 j further (8 KiB per sub-tile, 4 KiB per step), high half 8 rows more;
+    // v_swz depends on the row only modulo 4
+    const int row_off = jt * 8192 + j * 4096;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const char* base = reinterpret_cast<const char*>(vt) + lo.v[nt] + row_off;
+      // whole-vector casts only: __builtin_bit_cast of a vector element reads element 0
+      // whatever the index with this compiler, which loses the upper dword of each read
+      const u32x2 lov = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base)));
+      const u32x2 hiv = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 2048)));
+      const u32x4 w4 = {lov[0], lov[1], hiv[0], hiv[1]};
+      oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pf[j],
+                                                         oacc[nt], 0, 0, 0);
+    }
+  }
+}
+
+// Online softmax in the exp2 domain with a lazily raised reference. P = exp2(S scale_log2 -
+// m_run) is computed against the current reference m_run first; the reference is kept as long
+// as every lane's partial row sum over a sub-tile (16 probabilities) stays at or below
+// kSumLimit, which bounds every probability by it (fp32 O and l and bf16 P have ample range for
+// that). Only when a sub-tile breaks the bound, or the query has no finite reference yet, is
+// the exact sub-tile maximum taken, the reference raised to it, O and l rescaled and P
+// recomputed: on a query's first sub-tile and when its scores grow by more than about 2^12.
+// The row maximum is therefore never computed in the common case. Softmax does not depend on
+// the reference, and O and l always share it, so only the rounding differs from an eager
+// update. A query whose keys so far are all masked keeps m_run = -inf (O and l stay zero).
+constexpr float kSumLimit = 65536.f;
+
+// P of one sub-tile against the current reference, as bf16 B operands (pf[j] = keys
+// 16 j .. 16 j + 15 of the sub-tile in accumulator order), and the lane's partial row sum.
+__device__ __forceinline__ void softmax_sub(const f32x16& s, float scale_log2, float m_run,
+                                            bf16x8 (&pf)[2], float& psum) {
+  // masked keys of a query with no finite reference yet give exp2(-inf) = 0, not NaN
+  const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, mneg));
+    sum += p;
+    pf[r >> 3][r & 7] = (__bf16)p;
+  }
+  psum = sum;
+}
+
+// Accept the sub-tile's probabilities or, when a lane breaks the bound (see above), raise the
+// reference to the exact maximum, rescale O and l, and recompute them; then add the row sum.
+__device__ __forceinline__ void settle_sub(const f32x16& s, float scale_log2, float& m_run,
+                                           float& l_run, f32x16 (&oacc)[4], bf16x8 (&pf)[2],
+                                           float& psum) {
+  // !(x <= limit) is also true for NaN and +inf sums
+  if (__ballot(m_run == -INFINITY || !(psum <= kSumLimit)) != 0ull) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // lanes l32 and l32 + 32 hold the same query
     const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+    // exp2(-inf) = 0 for the first finite reference; -inf - -inf would be NaN
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[nt][r] *= alpha;
     m_run = m_new;
+    softmax_sub(s, scale_log2, m_run, pf, psum);
   }
-  float psum = 0.f;
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -m_run));
-      psum += p;
-      pf[2 * jt + (r >> 3)][r & 7] = (__bf16)p;
-    }
   l_run += psum;
-}
-
-// O^T += V^T P^T over one key tile; k step s covers keys 16 s .. 16 s + 15 in the accumulator
-// order of S^T, and V^T comes from the swizzled V tile through transposing LDS reads.
-__device__ __forceinline__ void pv_tile(const uint16_t* v_lds, const bf16x8 (&pf)[8], int h,
-                                        int tr_row, int tr_col, f32x16 (&oacc)[4]) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int jb = 16 * s + 4 * h + tr_row;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int col = 32 * nt + tr_col;
-      const int off_lo = jb * 128 + v_swz(jb, col >> 3) * 8 + (col & 7);
-      const int off_hi = (jb + 8) * 128 + v_swz(jb + 8, col >> 3) * 8 + (col & 7);
-      // whole-vector casts only: __builtin_bit_cast of a vector element reads element 0
-      // whatever the index with this compiler, which loses the upper dword of each read
-      const u32x2 lo = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_lo)));
-      const u32x2 hi = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_hi)));
-      const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-      oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pf[s],
-                                                         oacc[nt], 0, 0, 0);
-    }
-  }
 }
 
 // Pointers are separate __restrict__ parameters and the kept-block indices are staged in LDS:
@@ -198,6 +271,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const LdsOff loff = lds_offsets(l32, h, tr_row, tr_col);
 
   while (pos < end) {
     const int n = stage_list(col_idx, &pos, end, nkb, tail, list, wave_cnt, wave_cnt + 4, tid);
@@ -213,21 +287,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       // K(i) landed in every wave's part (V(i) may still be in flight)
       wait_vmcnt<8>();
       wg_barrier();
+      const LdsOff lo = lds_opaque(loff);
 
-      // S^T tiles: sacc[jt] covers keys 32 jt .. 32 jt + 31 (rows) x this wave's 32 queries
-      f32x16 sacc[4];
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
-        const int kr = 32 * jt + l32;
-        const uint16_t* krow = k_lds + kr * 128;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + k_swz(kr, 2 * s + h) * 8);
-          sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[jt], 0, 0, 0);
-        }
-      }
+      // sub-tiles u = 0 .. 3 of the block: the softmax of u runs next to the QK MFMAs of u + 1
+      // and the PV MFMAs of u - 1
+      f32x16 sa, sb;
+      bf16x8 pfa[2], pfb[2];
+      float psum;
+      qk_sub(k_lds, lo, qf, 0, sa);
+      softmax_sub(sa, scale_log2, m_run, pfa, psum);
+      qk_sub(k_lds, lo, qf, 1, sb);
+      settle_sub(sa, scale_log2, m_run, l_run, oacc, pfa, psum);
+
+      // V(i) landed (nothing else is in flight)
+      wait_vmcnt<0>();
+      wg_barrier();
+      softmax_sub(sb, scale_log2, m_run, pfb, psum);
+      qk_sub(k_lds, lo, qf, 2, sa);
+      pv_sub(v_lds, lo, pfa, 0, oacc);
+      settle_sub(sb, scale_log2, m_run, l_run, oacc, pfb, psum);
+
+      softmax_sub(sa, scale_log2, m_run, pfa, psum);
+      qk_sub(k_lds, lo, qf, 3, sb);
+      pv_sub(v_lds, lo, pfb, 1, oacc);
+      settle_sub(sa, scale_log2, m_run, l_run, oacc, pfa, psum);
+
       // the prefetch is unconditional (the last iteration re-fetches its own block): a
       // conditional DMA makes the compiler's wait bookkeeping drain all pending DMAs
       const int cb_next = __builtin_amdgcn_readfirstlane(list[more ? i + 1 : i]);
@@ -235,32 +319,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       wg_barrier();  // every wave is done reading K(i)
       tile_dma<false>(kbuf, cb_next * kTileK, k_lds, w, dmo, rbk);
 
-      bf16x8 pf[8];
-      softmax_tile(sacc, scale_log2, m_run, l_run, oacc, pf);
+      softmax_sub(sb, scale_log2, m_run, pfb, psum);
+      pv_sub(v_lds, lo, pfa, 2, oacc);
+      settle_sub(sb, scale_log2, m_run, l_run, oacc, pfb, psum);
+      pv_sub(v_lds, lo, pfb, 3, oacc);
 
-      // V(i) landed (the K prefetch just issued may still be in flight)
-      wait_vmcnt<8>();
-      wg_barrier();
-
-      // O^T += V^T P^T (written out here rather than through pv_tile: the same code behind a
-      // call made the compiler's LDS-DMA wait tracking add a drain of the K prefetch)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int jb = 16 * s + 4 * h + tr_row;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int col = 32 * nt + tr_col;
-          const int off_lo = jb * 128 + v_swz(jb, col >> 3) * 8 + (col & 7);
-          const int off_hi = (jb + 8) * 128 + v_swz(jb + 8, col >> 3) * 8 + (col & 7);
-          const u32x2 lo = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_lo)));
-          const u32x2 hi = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_lds + off_hi)));
-          const u32x4 w4 = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4),
-                                                             pf[s], oacc[nt], 0, 0, 0);
-        }
-      }
       wait_lgkmcnt0();
       wg_barrier();  // every wave is done reading V(i)
       tile_dma<true>(vbuf, cb_next * kTileV, v_lds, w, dmo, rbv);
@@ -280,25 +343,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     tile_load_partial<false>(kh + tok * ks.t, klast, k_lds, t_opaque, ks.t);
     tile_load_partial<true>(vh + tok * vs.t, klast, v_lds, t_opaque, vs.t);
     __syncthreads();
-    // tile bases offset by an opaque zero, so that the reads below do not share (and keep live
-    // through the main loop) the loop's precomputed LDS addresses
-    int zero = 0;
-    asm volatile("" : "+v"(zero));
-    const uint16_t* kt = k_lds + zero;
-    const uint16_t* vt = v_lds + zero;
-    f32x16 sacc[4];
-    qk_block(kt, qf, l32, h, sacc);
-    // opaque copies for the mask too: the 64 comparisons would otherwise be hoisted as well
+    const LdsOff lo = lds_opaque(loff);
+    // opaque copies for the mask too: the comparisons would otherwise be hoisted above the loop
     int h_opaque = h, klast_opaque = klast;
     asm volatile("" : "+v"(h_opaque), "+s"(klast_opaque));
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
+    for (int jt = 0; jt < 4; ++jt) {
+      f32x16 s;
+      qk_sub(k_lds, lo, qf, jt, s);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (sacc_key(jt, r, h_opaque) >= klast_opaque) sacc[jt][r] = -INFINITY;
-    bf16x8 pf[8];
-    softmax_tile(sacc, scale_log2, m_run, l_run, oacc, pf);
-    pv_tile(vt, pf, h, tr_row, tr_col, oacc);
+        if (sacc_key(jt, r, h_opaque) >= klast_opaque) s[r] = -INFINITY;
+      bf16x8 pf[2];
+      float psum;
+      softmax_sub(s, scale_log2, m_run, pf, psum);
+      settle_sub(s, scale_log2, m_run, l_run, oacc, pf, psum);
+      pv_sub(v_lds, lo, pf, jt, oacc);
+    }
   }
 
   // epilogue
