@@ -164,12 +164,22 @@ __device__ __forceinline__ void softmax_sub(const f32x16& s, float scale_log2, f
                                             bf16x8 (&pf)[2], float& psum) {
   // masked keys of a query with no finite reference yet give exp2(-inf) = 0, not NaN
   const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    pf[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, mneg));
+  // row sum of the bf16 probabilities that the PV product uses, two per v_dot2 (exact products
+  // by 1, fp32 accumulation): O is then normalised by the sum of its own weights
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   float sum = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, mneg));
-    sum += p;
-    pf[r >> 3][r & 7] = (__bf16)p;
+  for (int j = 0; j < 2; ++j) {
+    const u32x4 pw = __builtin_bit_cast(u32x4, pf[j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t dw = pw[i];  // a scalar copy: bit_cast of a vector element misreads
+      sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, dw), ones, sum, false);
+    }
   }
   psum = sum;
 }
