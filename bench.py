@@ -31,6 +31,11 @@ Reported numbers:
                   taken on the current kernel source (else null)
   cpu_baseline    the float64 NumPy oracle on the host cores, on a bounded sample of the same
                   workload, extrapolated to the whole step in the same unit
+
+Other suites (--suite): energy (token-level block energies), calibrate (energies + vote),
+anchor (the anchor-row path), ceiling (a dense 16384^3 bf16 GEMM through torch.matmul: the
+matrix-core throughput a tuned dense kernel sustains on this GPU, as context for the MFMA
+fraction).
 """
 from __future__ import annotations
 
@@ -62,7 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
-    ap.add_argument("--suite", choices=("hot", "energy", "calibrate", "anchor"), default="hot",
+    ap.add_argument("--suite", choices=("hot", "energy", "calibrate", "anchor", "ceiling"),
+                    default="hot",
                     help="hot: the selection + attention step (default); energy: the token-level "
                          "block energy, energy-driven selection and retained mass; calibrate: "
                          "per-input token-level masks voted into one static CSR, reused on a "
@@ -374,6 +380,38 @@ def anchor_suite(args, torch):
     print(json.dumps(res), flush=True)
 
 
+def ceiling_suite(args, torch):
+    """Context for the MFMA fraction: a dense bf16 GEMM of 16384^3 through torch.matmul (the
+    vendor's hipBLASLt kernels) timed the same way, i.e. the matrix-core throughput that a
+    tuned dense kernel sustains on this GPU under load, as a fraction of the nominal peak."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = 16384
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(max(args.warmup, 1)):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        torch.matmul(a, b, out=c)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    mean = sum(ms) / len(ms)
+    tflops = 2.0 * n ** 3 / (mean * 1e-3) / 1e12
+    res = {"metric": "dense bf16 GEMM TFLOP/s (torch.matmul, 16384^3): sustained MFMA context",
+           "value": round(tflops, 1), "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
+           "steps": args.steps, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "gemm_16384_cubed"}, "ms_mean": round(mean, 4),
+           "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
+
+
 def energy_cpu_baseline(w, q, k, flop, budget_s):
     """The oracle's Eq. (5) on as many rows of one head as fit in the budget, extrapolated."""
     import numpy as np
@@ -419,6 +457,8 @@ def main():
         return calibrate_suite(args, torch)
     if args.suite == "anchor":
         return anchor_suite(args, torch)
+    if args.suite == "ceiling":
+        return ceiling_suite(args, torch)
     import dynamic_block_sparse_pool_amd as dbsp
     from synth import BENCH_WORKLOAD, WORKLOADS, make_qkv
 
