@@ -11,7 +11,9 @@ density 0.09375). Prints one JSON line.
 Reported numbers:
   value           executed attention FLOP of the step / step time (TFLOP/s)
   select_ms       per-step time of the selection kernels (HIP events on the launch stream), mean
-                  of the timed steps; select_ms_p10/p50/p90 give the spread
+                  of the timed steps; select_ms_p10/p50/p90 give the spread. In mass mode it
+                  includes the longest-first row order that the attention launch then follows
+                  (--row-order)
   select_GBps     selection's algorithmic bytes (Q + K read once, CSR written) / select_ms
   attn_ms         per-step time of the attention kernel (HIP events on the launch stream), mean;
                   attn_ms_p10/p50/p90 give the spread
@@ -75,6 +77,9 @@ def parse():
                          "held-out input; anchor: the anchor-row path of repeating heads on "
                          "the DiT geometry (one JSON line each)")
     ap.add_argument("--inputs", type=int, default=16, help="calibrate: calibration inputs")
+    ap.add_argument("--row-order", choices=("auto", "row", "lpt"), default="auto",
+                    help="attention row order: longest first (lpt, built after each selection "
+                         "and timed with it) or row order; auto = lpt in mass mode")
     ap.add_argument("--only-copy", action="store_true",
                     help="run only the 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--cold-iters", type=int, default=8,
@@ -471,6 +476,10 @@ def main():
     plan = dbsp.SelectPlan(q, k, w.text, w.extra, **kw)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     idx = plan.run(q, k)
+    lpt = args.row_order == "lpt" or (args.row_order == "auto" and w.mode == "mass")
+    order = dbsp.lpt_order(q, k, idx) if lpt else None
+    order_ws = (torch.empty(8 * w.batch * w.heads * (w.n_k_blocks + 1) + 512, dtype=torch.uint8,
+                            device=dev) if lpt else None)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -481,9 +490,11 @@ def main():
         if e is not None:
             e[0].record(stream)
         plan.run(q, k)
+        if lpt:  # part of building the index: timed with the selection
+            dbsp.lpt_order(q, k, idx, out=order, workspace=order_ws)
         if e is not None:
             e[1].record(stream)
-        dbsp.sparse_attn_fwd(q, k, v, idx, out=out)
+        dbsp.sparse_attn_fwd(q, k, v, idx, out=out, row_order=order)
         if e is not None:
             e[2].record(stream)
 
@@ -554,7 +565,7 @@ def main():
             "head_dim": w.head_dim, "mode": w.mode, "param": w.param,
             "forced_text_blocks": list(w.text), "forced_extra_blocks": list(w.extra),
             "nnz": nnz, "executed_density": round(nnz / (rows * w.n_k_blocks), 5),
-            "output_dtype": "bf16",
+            "output_dtype": "bf16", "row_order": "lpt" if lpt else "row",
         },
         "select_ms": round(sel_ms, 4),
         "select_ms_p10": round(sp[0], 4), "select_ms_p50": round(sp[1], 4),

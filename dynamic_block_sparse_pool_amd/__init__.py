@@ -22,8 +22,8 @@ import torch
 from . import _abi
 from ._abi import DBSP_BLOCK, DbspError
 
-__all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "topk_budget", "select_nnz_bound",
-           "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
+__all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "lpt_order", "topk_budget",
+           "select_nnz_bound", "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
            "MaskVote", "anchor_attn_fwd", "to_intervals", "from_intervals",
            "DbspError", "DBSP_BLOCK", "version"]
 
@@ -234,12 +234,40 @@ def sparse_select(q: torch.Tensor, k: torch.Tensor, text_blocks: Tuple[int, int]
     return plan.run(q, k)
 
 
+def lpt_order(q: torch.Tensor, k: torch.Tensor, index: BlockIndex,
+              out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows of `index` in (batch, head) order, each head's rows sorted by kept count, longest
+    first (equal counts in an unspecified order): the row order for
+    sparse_attn_fwd(..., row_order=...). int32 [rows]."""
+    dims = _dims(q, k)
+    if index.row_ptr.numel() != dims.batch * dims.heads * _nblocks(dims.lq) + 1:
+        raise ValueError("index was built for a different shape")
+    if out is None:
+        out = torch.empty(index.rows, dtype=torch.int32, device=q.device)
+    elif out.shape != (index.rows,) or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [rows] tensor")
+    need = ctypes.c_uint64(0)
+    _abi.check(_abi.load().dbsp_row_order_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)),
+               "dbsp_row_order_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    st = _abi.load().dbsp_row_order_lpt(_ptr(index.row_ptr), ctypes.byref(dims),
+                                        index.col_idx.numel(), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(q.device))
+    _abi.check(st, "dbsp_row_order_lpt")
+    return out
+
+
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: BlockIndex,
                     softmax_scale: float = 0.0, out_dtype: Optional[torch.dtype] = None,
                     return_lse: bool = False, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None):
+                    lse: Optional[torch.Tensor] = None,
+                    row_order: Optional[torch.Tensor] = None):
     """Forward attention of every query block over the tokens of its kept key blocks only.
-    Returns O (and lse if return_lse)."""
+    Returns O (and lse if return_lse). row_order (int32 [rows], e.g. from lpt_order) sets the
+    order in which rows are started; it does not change the result."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_view(name, t)
     dims = _dims(q, k)
@@ -258,7 +286,17 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
     _check_view("out", out)
     if return_lse and lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    if all(t.is_contiguous() for t in (q, k, v, out)):
+    if row_order is not None:
+        if not all(t.is_contiguous() for t in (q, k, v, out)):
+            raise ValueError("row_order needs contiguous q, k, v and out")
+        if row_order.shape != (rows,) or row_order.dtype != torch.int32 or \
+                not row_order.is_contiguous() or row_order.device != q.device:
+            raise ValueError("row_order must be a contiguous int32 [rows] tensor on q's device")
+        st = _abi.load().dbsp_sparse_attn_fwd_ordered(
+            _ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), _ptr(index.row_ptr),
+            _ptr(index.col_idx), index.col_idx.numel(), float(softmax_scale), _ptr(out),
+            _dtype_code(out), _ptr(lse), _ptr(row_order), _stream(q.device))
+    elif all(t.is_contiguous() for t in (q, k, v, out)):
         st = _abi.load().dbsp_sparse_attn_fwd(
             _ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), _ptr(index.row_ptr),
             _ptr(index.col_idx), index.col_idx.numel(), float(softmax_scale), _ptr(out),

@@ -59,6 +59,10 @@ SIGNATURES = {
                                           _vp]),
     "dbsp_sparse_attn_fwd_strided": (_i32, [_vp, _PStr, _vp, _PStr, _vp, _PStr, _PDims, _vp, _vp,
                                             _i64, _f32, _vp, _PStr, _i32, _vp, _vp]),
+    "dbsp_sparse_attn_fwd_ordered": (_i32, [_vp, _vp, _vp, _PDims, _vp, _vp, _i64, _f32, _vp,
+                                            _i32, _vp, _vp, _vp]),
+    "dbsp_row_order_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
+    "dbsp_row_order_lpt": (_i32, [_vp, _PDims, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_sparse_select_list": (_i32, [_vp, _vp, _PDims, _vp, _i32, _i32, _f64, _i32, _f32,
                                        _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_select_nnz_bound_list": (_i32, [_PDims, _i32, _f64, _vp, _i32, _i32,

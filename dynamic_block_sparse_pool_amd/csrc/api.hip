@@ -434,7 +434,8 @@ static int32_t attn_impl(const void* q, const dbsp_strides* q_strides, const voi
                          const dbsp_strides* v_strides, const dbsp_dims* dims,
                          const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity,
                          float softmax_scale, void* o, const dbsp_strides* o_strides,
-                         int32_t o_dtype, float* lse_out, void* stream) {
+                         int32_t o_dtype, float* lse_out, const int32_t* row_order,
+                         void* stream) {
   if (!shape_ok(dims) || !q || !k || !v || !row_ptr || !o) return DBSP_ERR_INVALID_ARG;
   if (col_capacity < 0 || (col_capacity > 0 && !col_idx)) return DBSP_ERR_INVALID_ARG;
   if (o_dtype != DBSP_F32 && o_dtype != DBSP_BF16) return DBSP_ERR_INVALID_ARG;
@@ -483,6 +484,7 @@ static int32_t attn_impl(const void* q, const dbsp_strides* q_strides, const voi
   a.o = o;
   a.o_bf16 = o_dtype == DBSP_BF16;
   a.lse = lse_out;
+  a.row_order = row_order;
   if (dbsp::launch_attn(a, dims->head_dim, dims->dtype == DBSP_BF16,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return DBSP_ERR_HIP;
@@ -494,7 +496,46 @@ int32_t dbsp_sparse_attn_fwd(const void* q, const void* k, const void* v, const 
                              float softmax_scale, void* o, int32_t o_dtype, float* lse_out,
                              void* stream) {
   return attn_impl(q, nullptr, k, nullptr, v, nullptr, dims, row_ptr, col_idx, col_capacity,
-                   softmax_scale, o, nullptr, o_dtype, lse_out, stream);
+                   softmax_scale, o, nullptr, o_dtype, lse_out, nullptr, stream);
+}
+
+int32_t dbsp_sparse_attn_fwd_ordered(const void* q, const void* k, const void* v,
+                                     const dbsp_dims* dims, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int64_t col_capacity,
+                                     float softmax_scale, void* o, int32_t o_dtype,
+                                     float* lse_out, const int32_t* row_order, void* stream) {
+  if (!row_order) return DBSP_ERR_INVALID_ARG;
+  return attn_impl(q, nullptr, k, nullptr, v, nullptr, dims, row_ptr, col_idx, col_capacity,
+                   softmax_scale, o, nullptr, o_dtype, lse_out, row_order, stream);
+}
+
+int32_t dbsp_row_order_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes) {
+  if (!shape_ok(dims) || !bytes) return DBSP_ERR_INVALID_ARG;
+  // one int32 count per (batch, head, kept count) bucket (256-byte aligned), then one cursor per
+  // bucket and the total
+  const uint64_t nb = (uint64_t)dims->batch * (uint64_t)dims->heads * ((uint64_t)nkb_of(dims) + 1);
+  *bytes = ((4 * nb + 255) & ~(uint64_t)255) + 4 * (nb + 1);
+  return DBSP_OK;
+}
+
+int32_t dbsp_row_order_lpt(const int32_t* row_ptr, const dbsp_dims* dims, int64_t col_capacity,
+                           int32_t* order, void* workspace, uint64_t workspace_bytes,
+                           void* stream) {
+  if (!shape_ok(dims) || !row_ptr || !order || col_capacity < 0) return DBSP_ERR_INVALID_ARG;
+  if (rows_of(dims) > INT32_MAX) return DBSP_ERR_UNSUPPORTED;
+  uint64_t need = 0;
+  dbsp_row_order_workspace_bytes(dims, &need);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255))
+    return DBSP_ERR_WORKSPACE;
+  const uint64_t nb = (uint64_t)dims->batch * (uint64_t)dims->heads * ((uint64_t)nkb_of(dims) + 1);
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  int32_t* cursor = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                               ((4 * nb + 255) & ~(uint64_t)255));
+  if (dbsp::launch_row_order_lpt(row_ptr, col_capacity, rows_of(dims), nqb_of(dims),
+                                 nkb_of(dims), order, counts, cursor,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DBSP_ERR_HIP;
+  return DBSP_OK;
 }
 
 int32_t dbsp_sparse_attn_fwd_strided(const void* q, const dbsp_strides* q_strides, const void* k,
@@ -506,7 +547,7 @@ int32_t dbsp_sparse_attn_fwd_strided(const void* q, const dbsp_strides* q_stride
                                      float* lse_out, void* stream) {
   if (!q_strides || !k_strides || !v_strides || !o_strides) return DBSP_ERR_INVALID_ARG;
   return attn_impl(q, q_strides, k, k_strides, v, v_strides, dims, row_ptr, col_idx,
-                   col_capacity, softmax_scale, o, o_strides, o_dtype, lse_out, stream);
+                   col_capacity, softmax_scale, o, o_strides, o_dtype, lse_out, nullptr, stream);
 }
 
 int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, float softmax_scale,

@@ -224,13 +224,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ vg, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int64_t col_capacity, int nqb, int nkb, int64_t lq,
     int64_t lk, int heads, Strides qs, Strides ks, Strides vs, Strides os, float scale_log2,
-    void* __restrict__ o, int o_bf16, float* __restrict__ lse) {
+    void* __restrict__ o, int o_bf16, float* __restrict__ lse,
+    const int32_t* __restrict__ row_order, int64_t rows) {
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[kBlock * 128];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[kBlock * 128];
   __shared__ int list[kListCap];
   __shared__ int wave_cnt[8];
 
-  const int64_t row = blockIdx.x;
+  // the row of this workgroup (uniform): an entry of row_order outside [0, rows) does nothing
+  const int64_t row = row_order ? (int64_t)row_order[blockIdx.x] : (int64_t)blockIdx.x;
+  if (row < 0 || row >= rows) return;
   const int64_t bh = row / nqb;
   const int qb = (int)(row - bh * nqb);
   const int tid = threadIdx.x;
@@ -412,7 +415,9 @@ template <int D>
 __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   __shared__ float k_lds[kBlock][D];
   __shared__ float v_lds[kBlock][D];
-  const int64_t row = blockIdx.x;
+  // the row of this workgroup (uniform): an entry of row_order outside [0, rows) does nothing
+  const int64_t row = a.row_order ? (int64_t)a.row_order[blockIdx.x] : (int64_t)blockIdx.x;
+  if (row < 0 || row >= a.rows) return;
   const int64_t bh = row / a.nqb;
   const int qb = (int)(row - bh * a.nqb);
   const int t = threadIdx.x;
@@ -503,7 +508,8 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t s
     kern<<<grid, 256, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), a.row_ptr, a.col_idx, a.col_capacity, a.nqb, a.nkb,
-        a.lq, a.lk, a.heads, a.qs, a.ks, a.vs, a.os, a.scale_log2, a.o, a.o_bf16, a.lse);
+        a.lq, a.lk, a.heads, a.qs, a.ks, a.vs, a.os, a.scale_log2, a.o, a.o_bf16, a.lse,
+        a.row_order, a.rows);
   } else if (!bf16 && head_dim == 64)
     attn_fwd_f32_kernel<64><<<grid, 128, 0, stream>>>(a);
   else if (!bf16 && head_dim == 128)

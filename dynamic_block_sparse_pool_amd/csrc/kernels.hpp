@@ -65,6 +65,7 @@ struct AttnArgs {
   void* o;
   int o_bf16;
   float* lse;
+  const int32_t* row_order;  // nullable: workgroup b processes row row_order[b] (else row b)
 };
 
 struct EnergyArgs {
@@ -120,6 +121,9 @@ hipError_t launch_select_energy(const SelectArgs& a, const float* energy, hipStr
 hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream);
 // a.row_ptr = exclusive prefix of a.counts over a.n_rows rows (row_ptr[n_rows] = total)
 hipError_t launch_scan_counts(const SelectArgs& a, hipStream_t stream);
+// out[0 .. n] = exclusive prefix of counts[0 .. n) (out[n] = total); counts 256-byte aligned
+hipError_t launch_exclusive_scan(const int32_t* counts, int32_t* out, int64_t n,
+                                 hipStream_t stream);
 hipError_t launch_csr_to_intervals(const int32_t* row_ptr, const int32_t* col_idx,
                                    int64_t col_capacity, int nkb, int64_t rows, int32_t* iv_ptr,
                                    int32_t* iv, int64_t iv_capacity, int32_t* counts,
@@ -131,6 +135,11 @@ hipError_t launch_vote_accumulate(const int32_t* row_ptr, const int32_t* col_idx
                                   int64_t col_capacity, int nkb, int64_t rows, int32_t* counts,
                                   hipStream_t stream);
 hipError_t launch_anchor(const AnchorArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// order = the rows of each (batch, head) sorted by kept count, longest first, heads in order.
+// Workspace: nb = (rows / nqb) * (nkb + 1) bucket counts (256-byte aligned), then nb + 1 cursors.
+hipError_t launch_row_order_lpt(const int32_t* row_ptr, int64_t col_capacity, int64_t rows,
+                                int nqb, int nkb, int32_t* order, int32_t* counts,
+                                int32_t* cursor, hipStream_t stream);
 hipError_t launch_vote_select(const int32_t* counts, int n_inputs, double rho, const SelectArgs& a,
                               hipStream_t stream);
 

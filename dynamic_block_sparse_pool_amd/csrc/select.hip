@@ -605,9 +605,14 @@ __global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const 
   select_mass_probs<S>(a, p, row, lane);
 }
 
-hipError_t launch_scan_counts(const SelectArgs& a, hipStream_t stream) {
-  scan_counts_kernel<<<1, 1024, 0, stream>>>(a.counts, a.row_ptr, a.n_rows);
+hipError_t launch_exclusive_scan(const int32_t* counts, int32_t* out, int64_t n,
+                                 hipStream_t stream) {
+  scan_counts_kernel<<<1, 1024, 0, stream>>>(counts, out, n);
   return hipGetLastError();
+}
+
+hipError_t launch_scan_counts(const SelectArgs& a, hipStream_t stream) {
+  return launch_exclusive_scan(a.counts, a.row_ptr, a.n_rows, stream);
 }
 
 hipError_t launch_counts_to_csr(const SelectArgs& a, hipStream_t stream) {

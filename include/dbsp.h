@@ -247,6 +247,40 @@ int32_t dbsp_sparse_attn_fwd_strided(const void* q, const dbsp_strides* q_stride
                                      float* lse_out, void* stream);
 
 /*
+ * dbsp_sparse_attn_fwd with workgroup b processing row row_order[b] instead of row b, e.g. the
+ * longest-first order of dbsp_row_order_lpt. The order only decides which rows start first; each
+ * row's O and lse are the same as without it. row_order: device int32 [rows]; it should be a
+ * permutation of [0, rows): entries outside [0, rows) are skipped (their rows are not written)
+ * and a repeated entry computes its row twice. DBSP_ERR_INVALID_ARG for a NULL row_order, else
+ * as dbsp_sparse_attn_fwd.
+ */
+int32_t dbsp_sparse_attn_fwd_ordered(const void* q, const void* k, const void* v,
+                                     const dbsp_dims* dims, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int64_t col_capacity,
+                                     float softmax_scale, void* o, int32_t o_dtype,
+                                     float* lse_out, const int32_t* row_order, void* stream);
+
+/*
+ * Longest-first (LPT) row order for the attention launch, per head. With the cumulative-mass
+ * selection ([CalibAtt] key design 1) rows keep different numbers of key blocks; starting the
+ * longest rows first keeps a long row from starting last and leaving the GPU idle at the end.
+ *
+ * order (device int32 [rows], written) = the CSR rows in (batch, head) order, and within each
+ * (batch, head) sorted by kept count (row extents clipped to [0, col_capacity) as in
+ * dbsp_sparse_attn_fwd), longest first; rows of one head with equal counts appear in an
+ * unspecified order (the result is a permutation either way). Heads are not mixed, so the rows
+ * running together share one or two heads' K and V in the caches. workspace: device memory of
+ * at least dbsp_row_order_workspace_bytes bytes (about 8 bytes per (batch, head, kept count)),
+ * 256-byte aligned, overwritten. Enqueued on stream.
+ * Errors: DBSP_ERR_INVALID_ARG (NULL row_ptr / order, negative col_capacity, bad dims),
+ * DBSP_ERR_WORKSPACE, DBSP_ERR_UNSUPPORTED (more than 2^31 - 1 rows), DBSP_ERR_HIP.
+ */
+int32_t dbsp_row_order_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
+int32_t dbsp_row_order_lpt(const int32_t* row_ptr, const dbsp_dims* dims, int64_t col_capacity,
+                           int32_t* order, void* workspace, uint64_t workspace_bytes,
+                           void* stream);
+
+/*
  * Token-level block energy ([CalibAtt] key design 1, Eq. (5)).
  *
  * For each row r = (b, h, i) and each key block c of the same (b, h):

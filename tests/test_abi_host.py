@@ -346,3 +346,29 @@ def test_strided_calls_reject_bad_strides(lib):
     assert sel(ks=None) == E.DBSP_ERR_INVALID_ARG
     assert sel(qs=_abi.Strides(0, 3, 128)) == E.DBSP_ERR_INVALID_ARG
     assert sel() == E.DBSP_ERR_WORKSPACE      # valid strides reach the workspace check
+
+
+def test_row_order_calls_reject_bad_arguments(lib):
+    E = _abi
+    dims = _abi.Dims(1, 2, 256, 1000, 128, E.DBSP_BF16)   # 4 rows, 8 key blocks
+    need = ctypes.c_uint64(0)
+    assert lib.dbsp_row_order_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)) == E.DBSP_OK
+    assert need.value == 256 + 4 * (2 * 9 + 1)  # counts (aligned) + cursors, 2 heads x 9 buckets
+    assert lib.dbsp_row_order_workspace_bytes(None, ctypes.byref(need)) == E.DBSP_ERR_INVALID_ARG
+    assert lib.dbsp_row_order_workspace_bytes(ctypes.byref(dims), None) == E.DBSP_ERR_INVALID_ARG
+
+    def order(rp=FAKE, cap=16, out=FAKE, ws=FAKE, wsb=1 << 20):
+        return lib.dbsp_row_order_lpt(rp, ctypes.byref(dims), cap, out, ws, wsb, None)
+
+    for kw in ({"rp": None}, {"out": None}, {"cap": -1}):
+        assert order(**kw) == E.DBSP_ERR_INVALID_ARG, kw
+    assert order(ws=None) == E.DBSP_ERR_WORKSPACE
+    assert order(wsb=need.value - 1) == E.DBSP_ERR_WORKSPACE
+    assert order(ws=ctypes.c_void_p((1 << 20) + 64)) == E.DBSP_ERR_WORKSPACE  # not 256-aligned
+
+    def attn(row_order=FAKE, rp=FAKE):
+        return lib.dbsp_sparse_attn_fwd_ordered(FAKE, FAKE, FAKE, ctypes.byref(dims), rp, FAKE, 16,
+                                                0.0, FAKE, E.DBSP_F32, None, row_order, None)
+
+    assert attn(row_order=None) == E.DBSP_ERR_INVALID_ARG
+    assert attn(rp=None) == E.DBSP_ERR_INVALID_ARG

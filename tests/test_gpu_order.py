@@ -1,0 +1,78 @@
+"""Longest-first row order for the attention launch: the order is a permutation of the rows, heads
+in order, each head's rows with non-increasing kept counts (equal counts in any order), and
+attention started in that order gives bit-identical O and lse to attention started in row order
+(each row is computed by one workgroup with the same instructions whichever workgroup that is)."""
+import numpy as np
+import pytest
+import torch
+
+from synth import BLOCK, make_qkv, small_variants
+
+pytestmark = pytest.mark.gpu
+
+
+def dbsp():
+    import dynamic_block_sparse_pool_amd as m
+    return m
+
+
+def say(msg):
+    print(f"[gpu-order] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("name,lq", [("dit_mass_small", None), ("dit_mass_small", 19 * BLOCK - 48)])
+def test_lpt_order_and_ordered_attention(name, lq):
+    m = dbsp()
+    w = small_variants()[name]
+    if lq is not None:
+        w = w.with_(lq=lq, lk=lq)
+    say(f"case {name}: B={w.batch} H={w.heads} Lq={w.lq} Lk={w.lk} mass={w.param}")
+    q, k, v = make_qkv(w, device="cuda", seed=81)
+    idx = m.sparse_select(q, k, w.text, w.extra, mass=w.param)
+    order = m.lpt_order(q, k, idx)
+    torch.cuda.synchronize()
+    rp = idx.row_ptr.cpu().numpy().astype(np.int64)
+    counts = rp[1:] - rp[:-1]
+    o = order.cpu().numpy()
+    assert np.array_equal(np.sort(o), np.arange(idx.rows))          # a permutation
+    nqb = idx.n_q_blocks
+    head = o // nqb
+    assert (np.diff(head) >= 0).all()                                # heads in order
+    for hh in np.unique(head):
+        assert (np.diff(counts[o[head == hh]]) <= 0).all()           # longest first per head
+    assert len(np.unique(counts)) > 1                                # the case has unequal rows
+    o1, l1 = m.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32, return_lse=True)
+    o2, l2 = m.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32, return_lse=True,
+                               row_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_reversed_order_and_out_of_range_entries():
+    # any permutation gives the same result; entries outside [0, rows) leave their slot idle
+    m = dbsp()
+    w = small_variants()["final_small"]
+    say(f"case final_small reversed / out-of-range: H={w.heads} Lq={w.lq}")
+    q, k, v = make_qkv(w, device="cuda", seed=82)
+    idx = m.sparse_select(q, k, w.text, w.extra, density=w.param)
+    rows = idx.rows
+    rev = torch.arange(rows - 1, -1, -1, dtype=torch.int32, device="cuda")
+    o1 = m.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32)
+    o2 = m.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32, row_order=rev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    # drop the last row from the order: its output keeps the value it had before the call
+    part = rev.clone()
+    part[0] = rows + 5                                               # out of range: skipped
+    o3 = torch.full_like(o1, 7.0)
+    m.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32, row_order=part, out=o3)
+    torch.cuda.synchronize()
+    nqb = idx.n_q_blocks
+    last = rows - 1
+    b_h, i = divmod(last, nqb)
+    bb, hh = divmod(b_h, w.heads)
+    untouched = o3[bb, hh, i * BLOCK:(i + 1) * BLOCK]
+    assert torch.all(untouched == 7.0)
+    mask = torch.ones_like(o1, dtype=torch.bool)
+    mask[bb, hh, i * BLOCK:(i + 1) * BLOCK] = False
+    assert torch.equal(o3[mask], o1[mask])
