@@ -56,6 +56,7 @@ METRIC = "sparse-attn fwd ms + MFMA util @72k-token scale; select ms + HBM GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_final_720p.json")
 ATTN_SOURCES = ("attn.hip", "tile.hpp", "common.hpp", "kernels.hpp")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (the fp32 attention kernel is plain FMA)
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
@@ -474,7 +475,8 @@ def main():
     q, k, v = make_qkv(w, device=dev, seed=args.seed)
     kw = dict(density=w.param) if w.mode == "topk" else dict(mass=w.param)
     plan = dbsp.SelectPlan(q, k, w.text, w.extra, **kw)
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    bf16 = w.dtype == "bf16"
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
     idx = plan.run(q, k)
     lpt = args.row_order == "lpt" or (args.row_order == "auto" and w.mode == "mass")
     order = dbsp.lpt_order(q, k, idx) if lpt else None
@@ -565,7 +567,7 @@ def main():
             "head_dim": w.head_dim, "mode": w.mode, "param": w.param,
             "forced_text_blocks": list(w.text), "forced_extra_blocks": list(w.extra),
             "nnz": nnz, "executed_density": round(nnz / (rows * w.n_k_blocks), 5),
-            "output_dtype": "bf16", "row_order": "lpt" if lpt else "row",
+            "output_dtype": "bf16" if bf16 else "f32", "row_order": "lpt" if lpt else "row",
         },
         "select_ms": round(sel_ms, 4),
         "select_ms_p10": round(sp[0], 4), "select_ms_p50": round(sp[1], 4),
@@ -578,14 +580,18 @@ def main():
         "attn_ms_p10": round(ap_[0], 4), "attn_ms_p50": round(ap_[1], 4),
         "attn_ms_p90": round(ap_[2], 4),
         "attn_TFLOPs": round(att_tflops, 2),
-        "attn_mfma_frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_mfma_frac": round(att_tflops / PEAK_BF16_TFLOPS, 4) if bf16 else None,
         "attn_kv_GBps": round(att_gbps, 1),
         "attn_kv_hbm_frac": round(att_gbps / PEAK_HBM_GBPS, 4),
         "cold": cold,
-        "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_bf16_kernel",
-                     "per_launch_flop": exec_flop},
+        "roofline": ({"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                      "traffic": traffic, "kernel": "attn_fwd_bf16_kernel",
+                      "per_launch_flop": exec_flop} if bf16 else
+                     {"bound": "alu", "achieved": round(att_tflops, 4),
+                      "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(att_tflops / PEAK_F32_VALU_TFLOPS, 6), "traffic": None,
+                      "kernel": "attn_fwd_f32_kernel", "per_launch_flop": exec_flop}),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, idx.row_ptr, idx.col_idx, nnz,
