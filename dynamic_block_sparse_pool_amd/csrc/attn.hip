@@ -26,6 +26,8 @@
 //
 // attn_fwd_f32_kernel (fp32, head_dim 64 or 128): plain FMA arithmetic, one thread per query,
 // K and V blocks staged in LDS, online softmax in chunks of 32 keys.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -294,9 +296,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       tile_dma<false>(kbuf, cb * kTileK, k_lds, w, dmo, rbk);
       tile_dma<true>(vbuf, cb * kTileV, v_lds, w, dmo, rbv);
     }
-    for (int i = 0; i < n; ++i) {
-      const bool more = i + 1 < n;
-
+    // block i of the window; the last one (kLast) issues no prefetch, so no DMA is in flight
+    // when the window ends (an unconditional prefetch would re-fetch a block for nothing, and a
+    // conditional one makes the compiler's wait bookkeeping drain all pending DMAs)
+    auto block = [&](int i, auto last) {
+      constexpr bool kLast = decltype(last)::value;
       // K(i) landed in every wave's part (V(i) may still be in flight)
       wait_vmcnt<8>();
       wg_barrier();
@@ -325,22 +329,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       pv_sub(v_lds, lo, pfb, 1, oacc);
       settle_sub(sa, scale_log2, m_run, l_run, oacc, pfa, psum);
 
-      // the prefetch is unconditional (the last iteration re-fetches its own block): a
-      // conditional DMA makes the compiler's wait bookkeeping drain all pending DMAs
-      const int cb_next = __builtin_amdgcn_readfirstlane(list[more ? i + 1 : i]);
-      wait_lgkmcnt0();
-      wg_barrier();  // every wave is done reading K(i)
-      tile_dma<false>(kbuf, cb_next * kTileK, k_lds, w, dmo, rbk);
+      int cb_next = 0;
+      if (!kLast) {
+        cb_next = __builtin_amdgcn_readfirstlane(list[i + 1]);
+        wait_lgkmcnt0();
+        wg_barrier();  // every wave is done reading K(i)
+        tile_dma<false>(kbuf, cb_next * kTileK, k_lds, w, dmo, rbk);
+      }
 
       softmax_sub(sb, scale_log2, m_run, pfb, psum);
       pv_sub(v_lds, lo, pfa, 2, oacc);
       settle_sub(sb, scale_log2, m_run, l_run, oacc, pfb, psum);
       pv_sub(v_lds, lo, pfb, 3, oacc);
 
-      wait_lgkmcnt0();
-      wg_barrier();  // every wave is done reading V(i)
-      tile_dma<true>(vbuf, cb_next * kTileV, v_lds, w, dmo, rbv);
-    }
+      if (!kLast) {
+        wait_lgkmcnt0();
+        wg_barrier();  // every wave is done reading V(i)
+        tile_dma<true>(vbuf, cb_next * kTileV, v_lds, w, dmo, rbv);
+      }
+    };
+    for (int i = 0; i + 1 < n; ++i) block(i, std::false_type{});
+    block(n - 1, std::true_type{});
     wait_vmcnt<0>();
   }
 
