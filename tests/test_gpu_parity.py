@@ -211,6 +211,27 @@ def test_max_key_blocks():
     full_check_small(wm, seed=9)
 
 
+@pytest.mark.parametrize("lk", [2100 * BLOCK, 2100 * BLOCK - 50])
+def test_rows_longer_than_one_staging_window(lk):
+    # density 1: every row keeps all 2,100 key blocks, more than one LDS staging window of the
+    # attention kernel holds (2,048), so each row's list is staged and streamed in two windows;
+    # the ragged case also sends the partial last block through its own path after them
+    w = WORKLOADS["final_720p_clip2"].with_(name="two_windows", heads=1, lq=2 * BLOCK, lk=lk,
+                                             param=1.0, text=(0, 0))
+    # (selection stops at 2,048 key blocks; the attention takes any CSR, built here directly)
+    m = dbsp()
+    say(f"case two_windows: Lq={w.lq} Lk={w.lk}")
+    q, k, v = make_qkv(w, device="cuda", seed=12)
+    nkb = w.n_k_blocks
+    row_ptr = torch.arange(0, (w.rows + 1) * nkb, nkb, dtype=torch.int32, device="cuda")
+    col_idx = torch.arange(nkb, dtype=torch.int32, device="cuda").repeat(w.rows)
+    idx = m.BlockIndex(row_ptr=row_ptr, col_idx=col_idx, n_q_blocks=w.n_q_blocks, n_k_blocks=nkb)
+    o, lse = m.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    od, lsed = oracle.attention_dense(P.host(q), P.host(k), P.host(v))
+    P.check_attention(P.host(o), P.host(lse), od, lsed, True)
+
+
 def test_bf16_d64_select():
     w = small_variants()["star_mid_small"].with_(name="bf16_d64", head_dim=64)
     q, k, _ = make_qkv(w, device="cuda", seed=2)
