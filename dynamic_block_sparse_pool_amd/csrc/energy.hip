@@ -11,7 +11,8 @@
 // block_energy_bf16_kernel (bf16, head_dim 128): one workgroup of 4 waves per (batch, head,
 // query block) row, wave w owning queries [32 w, 32 w + 32) with the same S^T = K Q^T tiling on
 // 32x32x16 bf16 MFMAs as the attention kernel. Two sweeps over every key block of the head:
-//   1. running maximum and sum of exp2(s - m) per query, giving its log-sum-exp (log2 units);
+//   1. a running sum of exp2(s - m) per query against a lazily raised reference m, giving its
+//      log-sum-exp (log2 units);
 //   2. per key block, the sum of exp2(s - lse) over the block's 128 x 128 pairs: each lane adds
 //      its 64 values, the wave adds its lanes in a fixed DPP order, and the four wave totals are
 //      added in wave order and divided by 128 (deterministic, no atomics).
@@ -64,23 +65,47 @@ __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[4], int h, int klast) {
       if (sacc_key(jt, r, h) >= klast) sacc[jt][r] = -INFINITY;
 }
 
-// Sweep 1 on one S^T tile: running maximum and sum per query (log2 units).
-__device__ __forceinline__ void lse_update(const f32x16 (&sacc)[4], float scale_log2, float& m_run,
-                                           float& l_run) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(m_run, mx * scale_log2);
+// Sweep 1 on one S^T tile: running sum per query of exp2(s - m_run) against a lazily raised
+// reference m_run (log2 units). The tile's terms are added against the current reference
+// first; the reference is kept while every lane's partial sum over the tile (64 terms) stays at
+// or below kLseSumLimit, which bounds every term by it. Only when a tile breaks the bound, or the
+// query has no finite reference yet, is the exact tile maximum taken, the reference raised to it,
+// the running sum rescaled and the tile's terms recomputed: on the first tile and when the scores
+// grow by more than about 2^10. lse = m_run + log2(sum) does not depend on the reference, so
+// only the rounding differs from an eager update; the row maximum is not computed in the
+// common case.
+constexpr float kLseSumLimit = 65536.f;
+
+__device__ __forceinline__ float lse_terms(const f32x16 (&sacc)[4], float scale_log2,
+                                           float m_run) {
+  // masked keys of a query with no finite reference yet give exp2(-inf) = 0, not NaN
+  const float mneg = m_run == -INFINITY ? 0.f : -m_run;
   float ps = 0.f;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -m_new));
-  l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + ps;
-  m_run = m_new;
+    for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, mneg));
+  return ps;
+}
+
+__device__ __forceinline__ void lse_update(const f32x16 (&sacc)[4], float scale_log2, float& m_run,
+                                           float& l_run) {
+  float ps = lse_terms(sacc, scale_log2, m_run);
+  // !(x <= limit) is also true for NaN and +inf sums
+  if (__ballot(m_run == -INFINITY || !(ps <= kLseSumLimit)) != 0ull) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[jt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // lanes l32 and l32 + 32 hold the same query
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    // exp2(-inf) = 0 for the first finite reference; -inf - -inf would be NaN
+    l_run *= m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    ps = lse_terms(sacc, scale_log2, m_run);
+  }
+  l_run += ps;
 }
 
 // Sweep 2 on the S^T tile of key block c: the wave's probability total for c lands in lane
