@@ -18,10 +18,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
 // Round-to-nearest-even float -> bf16 bits (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -37,8 +33,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   if ((u << 1) == 0) u = 0;  // -0.0 -> +0.0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Number of set bits of `mask` in lanes below the calling lane.
 __device__ __forceinline__ int mbcnt64(uint64_t mask) {
@@ -140,12 +134,6 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
   return lane_u32(v, 63);
 }
 
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -153,18 +141,6 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
     uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
     v += ((uint64_t)hi << 32) | lo;
   }
-  return v;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
