@@ -1,0 +1,50 @@
+"""GPU parity on a seeded sweep of random small shapes, through the same checks as the named
+workloads: pooled scores, masks (bit-exact on the GPU's own scores), CSR, O and lse against
+the float64 oracle.
+
+Each case draws batch, heads, query and key lengths (mostly not multiples of 128, so the last
+query and key blocks are partial), the input dtype and head size, the forced ranges (text and
+extra, possibly empty), the rule (Top-K at a density or the cumulative mass at a threshold,
+including 1.0), the input structure and sometimes an explicit score scale. The draws come from
+a fixed NumPy generator, so the sweep is the same on every run.
+"""
+import numpy as np
+import pytest
+
+from synth import BLOCK, Workload
+from tests.test_gpu_parity import full_check_small, say
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def random_case(i: int):
+    rng = np.random.default_rng([20261203, i])
+    dtype = "bf16" if rng.random() < 0.7 else "f32"
+    head_dim = 128 if dtype == "bf16" else int(rng.choice([64, 128]))
+    batch = int(rng.choice([1, 1, 2]))
+    heads = int(rng.integers(1, 4))
+    lq = int(rng.integers(1, 13 * BLOCK))
+    lk = int(rng.integers(1, 24 * BLOCK))
+    nkb = -(-lk // BLOCK)
+    # forced ranges: text at the start (possibly empty), extra right after it (possibly empty)
+    t1 = int(rng.integers(0, min(4, nkb) + 1))
+    e_len = int(rng.integers(0, max(1, nkb - t1) // 2 + 1)) if rng.random() < 0.4 else 0
+    text, extra = (0, t1), (t1, t1 + e_len) if e_len else (0, 0)
+    if rng.random() < 0.6:
+        mode, param = "topk", float(rng.choice([0.03125, 0.1, 0.25, 0.5, 0.75, 1.0]))
+    else:
+        mode, param = "mass", float(rng.choice([0.3, 0.6, 0.9, 0.99, 1.0]))
+    structure = "centroid" if rng.random() < 0.75 else "iid"
+    score_scale = float(rng.choice([0.05, 0.2])) if rng.random() < 0.2 else None
+    w = Workload(f"random{i}", 100 + i, batch, heads, lq, lk, head_dim, dtype, text, extra, mode,
+                 param, structure)
+    return w, score_scale
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(i):
+    w, score_scale = random_case(i)
+    say(f"random case {i}: score_scale={score_scale}")
+    full_check_small(w, seed=500 + i, score_scale=score_scale)
