@@ -96,6 +96,16 @@ def _check_device_tensor(name: str, t: torch.Tensor) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_index(index: "BlockIndex", device: torch.device) -> None:
+    """row_ptr and col_idx: contiguous int32 tensors on `device` (the kernels read them)."""
+    for name, t in (("row_ptr", index.row_ptr), ("col_idx", index.col_idx)):
+        if t.device.type != device.type or (device.index is not None and
+                                            t.device.index != device.index):
+            raise ValueError(f"index.{name} must be on {device} (it is on {t.device})")
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"index.{name} must be a contiguous int32 tensor")
+
+
 def _check_view(name: str, t: torch.Tensor) -> None:
     """A 4-D GPU view whose last dimension is contiguous (other strides are passed through)."""
     if not t.is_cuda:
@@ -243,6 +253,7 @@ def lpt_order(q: torch.Tensor, k: torch.Tensor, index: BlockIndex,
     dims = _dims(q, k)
     if index.row_ptr.numel() != dims.batch * dims.heads * _nblocks(dims.lq) + 1:
         raise ValueError("index was built for a different shape")
+    _check_index(index, q.device)
     if out is None:
         out = torch.empty(index.rows, dtype=torch.int32, device=q.device)
     elif out.shape != (index.rows,) or out.dtype != torch.int32 or not out.is_contiguous():
@@ -278,6 +289,9 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
         raise ValueError("index was built for a different shape")
     if index.row_ptr.dtype != torch.int32 or index.col_idx.dtype != torch.int32:
         raise TypeError("row_ptr and col_idx must be int32")
+    _check_index(index, q.device)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     odt = out_dtype or (torch.float32 if q.dtype == torch.float32 else torch.bfloat16)
     if out is None:
         out = torch.empty(q.shape, dtype=odt, device=q.device)
@@ -349,6 +363,7 @@ def retained_mass(energy: torch.Tensor, index: BlockIndex, batch: int = 1, heads
     dims = _energy_dims(energy, batch, heads, index.n_k_blocks)
     if index.row_ptr.numel() != energy.shape[0] + 1:
         raise ValueError("index and energy have different row counts")
+    _check_index(index, energy.device)
     mass = torch.empty(energy.shape[0], dtype=torch.float64, device=energy.device)
     st = _abi.load().dbsp_retained_mass(_ptr(energy), ctypes.byref(dims), _ptr(index.row_ptr),
                                         _ptr(index.col_idx), index.col_idx.numel(), _ptr(mass),
@@ -400,6 +415,7 @@ class MaskVote:
     def add(self, index: BlockIndex) -> None:
         if index.row_ptr.numel() != self.rows + 1 or index.n_k_blocks != self.n_k_blocks:
             raise ValueError("mask shape differs from the vote's")
+        _check_index(index, self.device)
         st = _abi.load().dbsp_vote_accumulate(_ptr(index.row_ptr), _ptr(index.col_idx),
                                               index.col_idx.numel(), ctypes.byref(self.dims),
                                               _ptr(self.counts), _stream(self.device))
@@ -476,6 +492,9 @@ def to_intervals(index: BlockIndex, batch: int = 1, heads: int = 1):
     [capacity, 2] int32 [start, end) pairs; the first iv_ptr[-1] are used)."""
     dims = _index_dims(index, batch, heads)
     dev = index.row_ptr.device
+    if not index.row_ptr.is_cuda:
+        raise ValueError("index must be on a GPU")
+    _check_index(index, dev)
     rows = index.row_ptr.numel() - 1
     cap = rows * ((index.n_k_blocks + 1) // 2)
     iv_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)

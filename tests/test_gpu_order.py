@@ -76,3 +76,26 @@ def test_reversed_order_and_out_of_range_entries():
     mask = torch.ones_like(o1, dtype=torch.bool)
     mask[bb, hh, i * BLOCK:(i + 1) * BLOCK] = False
     assert torch.equal(o3[mask], o1[mask])
+
+
+def test_index_on_the_host_is_rejected():
+    # a CSR left in host memory must be refused before any launch (the kernels would read
+    # host addresses)
+    m = dbsp()
+    w = small_variants()["star_mid_small"]
+    q, k, v = make_qkv(w, device="cuda", seed=4)
+    idx = m.sparse_select(q, k, w.text, w.extra, density=w.param)
+    host = m.BlockIndex(idx.row_ptr.cpu(), idx.col_idx.cpu(), idx.n_q_blocks, idx.n_k_blocks)
+    with pytest.raises(ValueError):
+        m.sparse_attn_fwd(q, k, v, host)
+    with pytest.raises(ValueError):
+        m.lpt_order(q, k, host)
+    with pytest.raises(ValueError):
+        m.to_intervals(host, heads=w.heads)
+    vote = m.MaskVote(w.batch, w.heads, w.n_q_blocks, w.n_k_blocks, device="cuda")
+    with pytest.raises(ValueError):
+        vote.add(host)
+    # the same index on the GPU still runs
+    m.sparse_attn_fwd(q, k, v, idx)
+    vote.add(idx)
+    torch.cuda.synchronize()
