@@ -106,6 +106,12 @@ def _check_index(index: "BlockIndex", device: torch.device) -> None:
             raise ValueError(f"index.{name} must be a contiguous int32 tensor")
 
 
+def _check_on(name: str, t: torch.Tensor, device: torch.device) -> None:
+    """A caller-supplied output or workspace must live on the inputs' GPU."""
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (it is on {t.device})")
+
+
 def _check_view(name: str, t: torch.Tensor) -> None:
     """A 4-D GPU view whose last dimension is contiguous (other strides are passed through)."""
     if not t.is_cuda:
@@ -263,6 +269,10 @@ def lpt_order(q: torch.Tensor, k: torch.Tensor, index: BlockIndex,
                "dbsp_row_order_workspace_bytes")
     if workspace is None or workspace.numel() * workspace.element_size() < need.value:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    _check_on("out", out, q.device)
+    _check_on("workspace", workspace, q.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     st = _abi.load().dbsp_row_order_lpt(_ptr(index.row_ptr), ctypes.byref(dims),
                                         index.col_idx.numel(), _ptr(out), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
@@ -298,8 +308,14 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
     elif out.shape != q.shape or out.dtype != odt:
         raise ValueError("out has the wrong shape or dtype")
     _check_view("out", out)
+    _check_on("out", out, q.device)
     if return_lse and lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != q.shape[:3] or lse.dtype != torch.float32 or
+                              not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [batch, heads, Lq] tensor")
+    if lse is not None:
+        _check_on("lse", lse, q.device)
     if row_order is not None:
         if not all(t.is_contiguous() for t in (q, k, v, out)):
             raise ValueError("row_order needs contiguous q, k, v and out")
@@ -340,6 +356,7 @@ def block_energy(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0,
         out = torch.empty((rows, nkb), dtype=torch.float32, device=q.device)
     elif out.shape != (rows, nkb) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 [rows, n_k_blocks] tensor")
+    _check_on("out", out, q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     st = _abi.load().dbsp_block_energy(_ptr(q), _ptr(k), ctypes.byref(dims), float(softmax_scale),
                                        _ptr(out), _ptr(lse), _stream(q.device))
@@ -456,17 +473,22 @@ def anchor_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, frames: i
         out = torch.empty(q.shape, dtype=odt, device=q.device)
     elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
+    _check_on("out", out, q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     lib = _abi.load()
     n = ctypes.c_uint64()
     geom = (int(frames), int(rows_per_frame), int(row_width), int(n_anchors))
     _abi.check(lib.dbsp_anchor_workspace_bytes(ctypes.byref(dims), *geom, _dtype_code(out),
                                                ctypes.byref(n)), "dbsp_anchor_workspace_bytes")
-    if workspace is None or workspace.numel() < n.value:
+    if workspace is None or workspace.numel() * workspace.element_size() < n.value:
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    _check_on("workspace", workspace, q.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     st = lib.dbsp_anchor_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(dims), *geom,
                                   float(softmax_scale), _ptr(out), _dtype_code(out), _ptr(lse),
-                                  _ptr(workspace), workspace.numel(), _stream(q.device))
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(q.device))
     _abi.check(st, "dbsp_anchor_attn_fwd")
     return (out, lse) if return_lse else out
 

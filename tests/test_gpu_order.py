@@ -99,3 +99,21 @@ def test_index_on_the_host_is_rejected():
     m.sparse_attn_fwd(q, k, v, idx)
     vote.add(idx)
     torch.cuda.synchronize()
+
+
+def test_outputs_on_the_host_are_rejected():
+    m = dbsp()
+    w = small_variants()["star_mid_small"]
+    q, k, v = make_qkv(w, device="cuda", seed=5)
+    idx = m.sparse_select(q, k, w.text, w.extra, density=w.param)
+    with pytest.raises(ValueError):
+        m.sparse_attn_fwd(q, k, v, idx, return_lse=True,
+                          lse=torch.empty(q.shape[:3], dtype=torch.float32))
+    with pytest.raises(ValueError):  # wrong lse shape
+        m.sparse_attn_fwd(q, k, v, idx, return_lse=True,
+                          lse=torch.empty(q.shape[:2], dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        m.block_energy(q, k, out=torch.empty((w.rows, w.n_k_blocks), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        m.lpt_order(q, k, idx, out=torch.empty(w.rows, dtype=torch.int32))
+    torch.cuda.synchronize()
