@@ -71,6 +71,8 @@ def _dims(q: torch.Tensor, k: torch.Tensor) -> _abi.Dims:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} vs k {tuple(k.shape)}")
     if q.dtype != k.dtype:
         raise TypeError("q and k must share a dtype")
+    if q.device != k.device:
+        raise ValueError("q and k must be on one device")
     return _abi.Dims(q.shape[0], q.shape[1], q.shape[2], k.shape[2], q.shape[3], _dtype_code(q))
 
 
@@ -539,6 +541,11 @@ def from_intervals(iv_ptr: torch.Tensor, iv: torch.Tensor, n_q_blocks: int, n_k_
     rows = batch * heads * n_q_blocks
     if iv_ptr.numel() != rows + 1:
         raise ValueError("iv_ptr has the wrong length")
+    _check_device_tensor("iv_ptr", iv_ptr)
+    _check_device_tensor("iv", iv)
+    _check_on("iv", iv, dev)
+    if iv_ptr.dtype != torch.int32 or iv.dtype != torch.int32 or iv.dim() != 2 or iv.shape[1] != 2:
+        raise ValueError("iv_ptr must be int32 [rows + 1] and iv int32 [capacity, 2]")
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(max(rows * n_k_blocks, 1), dtype=torch.int32, device=dev)
     ws = _skiplist_workspace(dims, dev)
