@@ -17,6 +17,17 @@ What it computes, step by step, in the order the pages describe:
 
 Every function cites the passage it follows by page title and section. Readings taken where the
 pages are silent are listed in the docstrings of the functions that make them.
+
+Parity unpinned against the pages: every function here is pinned by tests to closed forms,
+brute force, library routines or hand-worked rows of its own definition, but for these readings
+no value printed on the pages confirms that the definition is the pages' intent:
+  topk_budget     K = ceil(density * |C|) over the non-forced blocks (floor or round would keep
+                  one block fewer on some configurations)
+  select_mass     forced blocks counted toward the threshold first (no configuration on the
+                  pages has forced blocks in mass mode)
+  anchor_rows     equally spaced anchors read as band centres floor((2 j + 1) H / (2 k))
+and, for the workloads rather than a function, the 48 padding tokens of the 21 x 3,600 DiT
+sequence read as ordinary tokens.
 """
 from .select import (BLOCK, MASS_BITS, block_scores, block_softmax, forced_blocks, mass_threshold_units,
                      mass_units, n_blocks, pool, select_mass, select_topk, sparse_select, to_csr, to_intervals,
