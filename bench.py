@@ -31,6 +31,10 @@ Reported numbers:
                   against the bf16 dense MFMA peak; traffic = its HBM bytes per launch from the
                   committed FETCH_SIZE / WRITE_SIZE counter summary, when that summary was
                   taken on the current kernel source (else null)
+  gemm_ceiling    context for the MFMA fraction, measured after the timed region: a dense
+                  bf16 16384^3 GEMM through torch.matmul (the vendor's hipBLASLt) on the same
+                  GPU, its TFLOP/s, fraction of the nominal peak, and attention's throughput as
+                  a fraction of it (--no-ceiling skips it)
   cpu_baseline    the float64 NumPy oracle on the host cores, on a bounded sample of the same
                   workload, extrapolated to the whole step in the same unit
 
@@ -68,6 +72,8 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the dense-GEMM context figure (gemm_ceiling) of the hot suite")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle's attention sample")
     ap.add_argument("--suite", choices=("hot", "energy", "calibrate", "anchor", "ceiling"),
@@ -386,22 +392,23 @@ def anchor_suite(args, torch):
     print(json.dumps(res), flush=True)
 
 
-def ceiling_suite(args, torch):
-    """Context for the MFMA fraction: a dense bf16 GEMM of 16384^3 through torch.matmul (the
-    vendor's hipBLASLt kernels) timed the same way, i.e. the matrix-core throughput that a
-    tuned dense kernel sustains on this GPU under load, as a fraction of the nominal peak."""
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    n = 16384
+GEMM_N = 16384
+
+
+def gemm_ceiling(torch, dev, seed, steps, warmup):
+    """Mean time and TFLOP/s of a dense bf16 GEMM of GEMM_N^3 through torch.matmul (the vendor's
+    hipBLASLt kernels), timed with HIP events: the matrix-core throughput a tuned dense kernel
+    sustains on this GPU under load. Context for the MFMA fraction, not part of the hot path."""
+    n = GEMM_N
     g = torch.Generator(device=dev)
-    g.manual_seed(args.seed)
+    g.manual_seed(seed)
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
     c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
-    for _ in range(max(args.warmup, 1)):
+    for _ in range(max(warmup, 1)):
         torch.matmul(a, b, out=c)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for e in ev:
         e[0].record()
         torch.matmul(a, b, out=c)
@@ -409,7 +416,15 @@ def ceiling_suite(args, torch):
     torch.cuda.synchronize()
     ms = [e[0].elapsed_time(e[1]) for e in ev]
     mean = sum(ms) / len(ms)
-    tflops = 2.0 * n ** 3 / (mean * 1e-3) / 1e12
+    del a, b, c
+    return mean, 2.0 * n ** 3 / (mean * 1e-3) / 1e12
+
+
+def ceiling_suite(args, torch):
+    """Context for the MFMA fraction: the dense bf16 GEMM of gemm_ceiling as its own line."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mean, tflops = gemm_ceiling(torch, dev, args.seed, args.steps, args.warmup)
     res = {"metric": "dense bf16 GEMM TFLOP/s (torch.matmul, 16384^3): sustained MFMA context",
            "value": round(tflops, 1), "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
            "steps": args.steps, "dtype": "bf16", "data": "synthetic",
@@ -593,6 +608,12 @@ def main():
                       "frac": round(att_tflops / PEAK_F32_VALU_TFLOPS, 6), "traffic": None,
                       "kernel": "attn_fwd_f32_kernel", "per_launch_flop": exec_flop}),
     }
+    if bf16 and not args.no_ceiling:
+        g_ms, g_tflops = gemm_ceiling(torch, dev, args.seed, 5, 1)
+        res["gemm_ceiling"] = {
+            "what": f"dense bf16 GEMM {GEMM_N}^3 through torch.matmul (hipBLASLt) on this GPU",
+            "TFLOPs": round(g_tflops, 1), "frac_of_peak": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+            "attn_frac_of_gemm": round(att_tflops / g_tflops, 4)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, idx.row_ptr, idx.col_idx, nnz,
                                            flop_per_pair, args.cpu_seconds)
