@@ -11,6 +11,7 @@ import oracle.attention as oatt
 import oracle.energy as oen
 import oracle.anchor as oanc
 import oracle.select as osel
+import oracle.vote as ovote
 from tests import test_oracle_pins as pins
 
 
@@ -99,6 +100,83 @@ def _softmax_weighted_unnormalised(logits, values):
     return e @ values, (m + np.log(e.sum(axis=-1, keepdims=True)))[..., 0]
 
 
+def _pool_sum(x, block=oracle.BLOCK):
+    # block sums instead of block means
+    x = np.asarray(x, np.float64)
+    return osel._orig_pool(x, block) * np.array(
+        [len(osel.block_tokens(i, x.shape[-2], block)) for i in range(osel.n_blocks(x.shape[-2],
+                                                                                   block))])[:, None]
+
+
+def _pool_partial_by_block(x, block=oracle.BLOCK):
+    # a partial last block divided by the full block size
+    x = np.asarray(x, np.float64)
+    out = osel._orig_pool(x, block)
+    n_last = len(osel.block_tokens(out.shape[-2] - 1, x.shape[-2], block))
+    out[..., -1, :] *= n_last / block
+    return out
+
+
+def _pool_across_heads(x, block=oracle.BLOCK):
+    # pooled over the heads as well (a shared mean for every head)
+    out = osel._orig_pool(x, block)
+    if out.ndim >= 3:
+        out = np.broadcast_to(out.mean(axis=-3, keepdims=True), out.shape).copy()
+    return out
+
+
+def _attention_rows_unscaled(q, k, v, row_ptr, col_idx, rows=None, scale=None, block=oracle.BLOCK):
+    # the 1/sqrt(d) logit scale left out
+    return oatt._orig_attention_rows(q, k, v, row_ptr, col_idx, rows,
+                                     1.0 if scale is None else scale, block)
+
+
+def _topk_without_forced(scores, forced, k):
+    # the forced blocks are not added to the kept set
+    kept = osel._orig_select_topk(scores, forced, k)
+    kept[..., forced] = False
+    return kept
+
+
+def _topk_forced_count_toward_k(scores, forced, k):
+    # the forced blocks use up part of the Top-K budget
+    return osel._orig_select_topk(scores, forced, max(k - int(np.sum(forced)), 0))
+
+
+def _mass_candidates_only(p, forced, tau):
+    # energies renormalised over the candidate blocks before the prefix is taken
+    p = np.asarray(p, np.float64)
+    c = np.where(forced, 0.0, p)
+    total = c.sum(axis=-1, keepdims=True)
+    c = np.divide(c, total, out=np.zeros_like(c), where=total > 0)
+    return osel._orig_select_mass(np.where(forced, p, c), forced, tau)
+
+
+def _csr_descending(kept):
+    row_ptr, col_idx = osel._orig_to_csr(kept)
+    col_idx = col_idx.copy()
+    for r in range(row_ptr.size - 1):
+        col_idx[row_ptr[r]:row_ptr[r + 1]] = col_idx[row_ptr[r]:row_ptr[r + 1]][::-1]
+    return row_ptr, col_idx
+
+
+def _csr_inclusive_ptr(kept):
+    row_ptr, col_idx = osel._orig_to_csr(kept)
+    return np.concatenate([row_ptr[1:], row_ptr[-1:]]), col_idx
+
+
+def _vote_strict(masks, rho):
+    masks = np.asarray(masks, dtype=bool)
+    return masks.mean(axis=0) > rho
+
+
+def _intervals_closed(kept):
+    ptr, iv = osel._orig_to_intervals(kept)
+    iv = iv.copy()
+    iv[:, 1] -= 1
+    return ptr, iv
+
+
 MUTATIONS = {
     "scores without 1/sqrt(d)": (osel, "block_scores", _scores_unscaled,
                                  [pins.test_scores_closed_form_asymmetric, pins.test_mean_field_identity]),
@@ -126,6 +204,25 @@ MUTATIONS = {
     "upper bound one token short": (oen, "token_upper_bound", _upper_bound_off_by_one,
                                     [pins.test_token_upper_bound_brute_force_and_bounds,
                                      pins.test_token_upper_bound_mean_field_equals_block_topk]),
+    "pool sums instead of averaging": (osel, "pool", _pool_sum, [pins.test_pool_closed_form]),
+    "partial block divided by 128": (osel, "pool", _pool_partial_by_block,
+                                     [pins.test_pool_partial_block_closed_form]),
+    "pool across heads": (osel, "pool", _pool_across_heads, [pins.test_pool_keeps_heads_apart]),
+    "attention without 1/sqrt(d)": (oatt, "attention_rows", _attention_rows_unscaled,
+                                    [pins.test_partial_blocks_match_sdpa_and_sum_to_one]),
+    "Top-K leaves the forced blocks out": (osel, "select_topk", _topk_without_forced,
+                                           [pins.test_topk_golden]),
+    "forced blocks use up the Top-K budget": (osel, "select_topk", _topk_forced_count_toward_k,
+                                              [pins.test_topk_golden]),
+    "mass renormalised over candidates": (osel, "select_mass", _mass_candidates_only,
+                                          [pins.test_mass_golden,
+                                           pins.test_mass_forced_energy_is_not_renormalised]),
+    "CSR columns descending": (osel, "to_csr", _csr_descending, [pins.test_csr_closed_form]),
+    "CSR row pointers inclusive": (osel, "to_csr", _csr_inclusive_ptr,
+                                   [pins.test_csr_closed_form]),
+    "vote uses strict >": (ovote, "vote_masks", _vote_strict, [pins.test_vote_worked_example]),
+    "intervals closed at the end": (osel, "to_intervals", _intervals_closed,
+                                    [pins.test_intervals_hand_example_and_round_trip]),
 }
 
 

@@ -234,6 +234,17 @@ def test_mass_golden():
         assert np.flatnonzero(kept).tolist() == case["kept"], case["name"]
 
 
+def test_mass_forced_energy_is_not_renormalised():
+    # The energies are the row's softmax over all key blocks; forced blocks keep theirs and the
+    # candidates are not rescaled to the non-forced share. p = (0.5, 0.2, 0.2, 0.1) with block 0
+    # forced and tau = 0.8: 0.5 + 0.2 = 0.7 < 0.8, so two candidates are needed (0.9). Rescaling
+    # the candidates by 1 / 0.5 would give 0.5 + 0.4 = 0.9 with one.
+    p = np.array([[0.5, 0.2, 0.2, 0.1]])
+    forced = np.array([True, False, False, False])
+    kept = oracle.select_mass(p, forced, 0.8)[0]
+    assert np.flatnonzero(kept).tolist() == [0, 1, 2]
+
+
 def test_mass_units_exact():
     assert int(oracle.mass_units(np.array([0.5]))[0]) == 2 ** 61
     assert int(oracle.mass_units(np.array([2.0 ** -62]))[0]) == 1
