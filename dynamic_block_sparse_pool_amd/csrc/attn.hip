@@ -24,8 +24,9 @@
 //     accumulator layout of S^T).
 // Epilogue: O = O^T / l, written in fp32 or bf16, and lse = ln 2 * (m + log2 l).
 //
-// attn_fwd_f32_kernel (fp32, head_dim 64 or 128): plain FMA arithmetic, one thread per query,
-// K and V blocks staged in LDS, online softmax in chunks of 32 keys.
+// attn_fwd_f32_kernel (fp32, head_dim 64 or 128): plain FMA arithmetic, four lanes per query
+// (a quarter of the head dimension each), K and V blocks staged in LDS, online softmax in
+// chunks of 32 keys.
 #include <type_traits>
 
 #include "common.hpp"
@@ -420,29 +421,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     lse[qtok] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
+// fp32 path: one workgroup of 512 threads per CSR row. Each query of the block is served by a
+// quad of consecutive lanes; lane `part` of the quad holds dims [part * D / 4, (part + 1) * D / 4)
+// of the query and of its output accumulator. A key's logit is the sum of the four partial dot
+// products (two quad shuffles, the same bits in all four lanes), so the softmax state (m, l) is
+// replicated in the quad and each lane updates its quarter of O.
 template <int D>
-__global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
-  __shared__ float k_lds[kBlock][D];
-  __shared__ float v_lds[kBlock][D];
+__global__ __launch_bounds__(512) void attn_fwd_f32_kernel(AttnArgs a) {
+  constexpr int kPart = D / 4;   // dims per lane
+  constexpr int kVecs = kPart / 4;
+  __shared__ __attribute__((aligned(16))) float k_lds[kBlock * D];
+  __shared__ __attribute__((aligned(16))) float v_lds[kBlock * D];
   // the row of this workgroup (uniform): an entry of row_order outside [0, rows) does nothing
   const int64_t row = a.row_order ? (int64_t)a.row_order[blockIdx.x] : (int64_t)blockIdx.x;
   if (row < 0 || row >= a.rows) return;
   const int64_t bh = row / a.nqb;
   const int qb = (int)(row - bh * a.nqb);
   const int t = threadIdx.x;
-  const int64_t qi = (int64_t)qb * kBlock + t;
+  const int part = t & 3;
+  const int64_t qi = (int64_t)qb * kBlock + (t >> 2);
   const bool q_valid = qi < a.lq;
   const int64_t qtok = bh * a.lq + (q_valid ? qi : 0);  // lse index (contiguous)
-  const float* qp = static_cast<const float*>(a.q) + token_offset(a.qs, bh, a.heads, q_valid ? qi : 0);
+  const float* qp = static_cast<const float*>(a.q) +
+                    token_offset(a.qs, bh, a.heads, q_valid ? qi : 0) + part * kPart;
   const float* kp = static_cast<const float*>(a.k) + token_offset(a.ks, bh, a.heads, 0);
   const float* vp = static_cast<const float*>(a.v) + token_offset(a.vs, bh, a.heads, 0);
 
-  float qv[D];
+  float qv[kPart], acc[kPart];
 #pragma unroll
-  for (int d = 0; d < D; ++d) qv[d] = q_valid ? qp[d] : 0.f;
-  float acc[D];
+  for (int c = 0; c < kVecs; ++c) {
+    const f32x4 x = q_valid ? *reinterpret_cast<const f32x4*>(qp + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    for (int e = 0; e < 4; ++e) qv[4 * c + e] = x[e];
+  }
+#pragma unroll
+  for (int d = 0; d < kPart; ++d) acc[d] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
   int64_t beg = a.row_ptr[row], end = a.row_ptr[row + 1];
@@ -457,11 +470,14 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
                                                                  : kBlock);
     const float* kb = kp + (int64_t)cb * kBlock * a.ks.t;
     const float* vb = vp + (int64_t)cb * kBlock * a.vs.t;
-    for (int i = t; i < kBlock * D; i += 128) {
-      const int r = i / D, col = i - (i / D) * D;
+    for (int i = t; i < kBlock * D / 4; i += 512) {
+      const int r = i / (D / 4), c4 = i - r * (D / 4);
       const bool in = r < valid;
-      (&k_lds[0][0])[i] = in ? kb[r * a.ks.t + col] : 0.f;
-      (&v_lds[0][0])[i] = in ? vb[r * a.vs.t + col] : 0.f;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      reinterpret_cast<f32x4*>(k_lds)[i] =
+          in ? *reinterpret_cast<const f32x4*>(kb + r * a.ks.t + 4 * c4) : z;
+      reinterpret_cast<f32x4*>(v_lds)[i] =
+          in ? *reinterpret_cast<const f32x4*>(vb + r * a.vs.t + 4 * c4) : z;
     }
     __syncthreads();
     for (int j0 = 0; j0 < valid; j0 += 32) {
@@ -469,9 +485,16 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
+        const float* kr = k_lds + (j0 + j) * D + part * kPart;
         float dot = 0.f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) dot = fmaf(qv[d], k_lds[j0 + j][d], dot);
+        for (int c = 0; c < kVecs; ++c) {
+          const f32x4 kk = *reinterpret_cast<const f32x4*>(kr + 4 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = fmaf(qv[4 * c + e], kk[e], dot);
+        }
+        dot += __shfl_xor(dot, 1, 64);
+        dot += __shfl_xor(dot, 2, 64);
         s[j] = j0 + j < valid ? dot * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[j]);
       }
@@ -479,13 +502,18 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] *= alpha;
+      for (int d = 0; d < kPart; ++d) acc[d] *= alpha;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const float p = __builtin_amdgcn_exp2f(s[j] - m_new);
         l_run += p;
+        const float* vr = v_lds + (j0 + j) * D + part * kPart;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = fmaf(p, v_lds[j0 + j][d], acc[d]);
+        for (int c = 0; c < kVecs; ++c) {
+          const f32x4 vv = *reinterpret_cast<const f32x4*>(vr + 4 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * c + e] = fmaf(p, vv[e], acc[4 * c + e]);
+        }
       }
       m_run = m_new;
     }
@@ -493,17 +521,23 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnArgs a) {
   }
   if (!q_valid) return;
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  const int64_t otok = token_offset(a.os, bh, a.heads, qi);
+  const int64_t otok = token_offset(a.os, bh, a.heads, qi) + part * kPart;
   if (a.o_bf16) {
     uint16_t* orow = static_cast<uint16_t*>(a.o) + otok;
 #pragma unroll
-    for (int d = 0; d < D; ++d) orow[d] = (uint16_t)f32_to_bf16_bits(acc[d] * inv);
+    for (int d = 0; d < kPart; ++d) orow[d] = (uint16_t)f32_to_bf16_bits(acc[d] * inv);
   } else {
     float* orow = static_cast<float*>(a.o) + otok;
 #pragma unroll
-    for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+    for (int c = 0; c < kVecs; ++c) {
+      f32x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = acc[4 * c + e] * inv;
+      *reinterpret_cast<f32x4*>(orow + 4 * c) = ov;
+    }
   }
-  if (a.lse) a.lse[qtok] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+  if (a.lse && part == 0)
+    a.lse[qtok] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t stream) {
@@ -520,9 +554,9 @@ hipError_t launch_attn(const AttnArgs& a, int head_dim, bool bf16, hipStream_t s
         a.lq, a.lk, a.heads, a.qs, a.ks, a.vs, a.os, a.scale_log2, a.o, a.o_bf16, a.lse,
         a.row_order, a.rows);
   } else if (!bf16 && head_dim == 64)
-    attn_fwd_f32_kernel<64><<<grid, 128, 0, stream>>>(a);
+    attn_fwd_f32_kernel<64><<<grid, 512, 0, stream>>>(a);
   else if (!bf16 && head_dim == 128)
-    attn_fwd_f32_kernel<128><<<grid, 128, 0, stream>>>(a);
+    attn_fwd_f32_kernel<128><<<grid, 512, 0, stream>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

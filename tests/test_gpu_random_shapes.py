@@ -5,8 +5,9 @@ the float64 oracle.
 Each case draws batch, heads, query and key lengths (mostly not multiples of 128, so the last
 query and key blocks are partial), the input dtype and head size, the forced ranges (text and
 extra, possibly empty), the rule (Top-K at a density or the cumulative mass at a threshold,
-including 1.0), the input structure and sometimes an explicit score scale. The draws come from
-a fixed NumPy generator, so the sweep is the same on every run.
+including 1.0), the input structure (block centroids or unit-variance noise; always the latter
+for fp32, the distribution its 1e-5 bound is stated for) and sometimes an explicit score scale.
+The draws come from a fixed NumPy generator, so the sweep is the same on every run.
 """
 import numpy as np
 import pytest
@@ -37,6 +38,11 @@ def random_case(i: int):
     else:
         mode, param = "mass", float(rng.choice([0.3, 0.6, 0.9, 0.99, 1.0]))
     structure = "centroid" if rng.random() < 0.75 else "iid"
+    if dtype == "f32":
+        # the 1e-5 bound on fp32 outputs is stated for unit-variance inputs (logits of order 1);
+        # block-centroid inputs give logits near 100, where the rounding of one fp32 dot product
+        # alone moves O by about 1e-5, whatever the kernel
+        structure = "iid"
     score_scale = float(rng.choice([0.05, 0.2])) if rng.random() < 0.2 else None
     w = Workload(f"random{i}", 100 + i, batch, heads, lq, lk, head_dim, dtype, text, extra, mode,
                  param, structure)
