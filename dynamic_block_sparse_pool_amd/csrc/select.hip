@@ -22,8 +22,9 @@
 //   block 64 e + l), maps scores to order-preserving uint32 keys and finds the selection
 //   threshold T most significant bits first: in Top-K mode by radix select on bytes with a
 //   per-wave LDS histogram (stopping when a bucket holds exactly the remaining count), in mass
-//   mode by a bitwise search on 64-bit mass sums that starts below the common high bits of the
-//   smallest and largest candidate key (T lies between them). Keys above T are kept, and keys
+//   mode by radix search on bytes with a per-wave LDS histogram of 64-bit fixed-point masses,
+//   starting at the first byte where the smallest and largest candidate keys differ (T lies
+//   between them). Keys above T are kept, and keys
 //   equal to T in ascending block order until the count (Top-K) or mass (mass mode) is met:
 //   the same set as the prefix of a stable (value desc, index asc) sort. Kept flags are
 //   emitted slot by slot with mbcnt, so col_idx comes out ascending.
@@ -358,11 +359,57 @@ __device__ __forceinline__ void select_topk_row(const SelectArgs& a, const float
   }
 }
 
+// Radix step of the mass threshold search. Among the candidate keys that share the already
+// decided high bits `prefix` (bits above shift + 8), add their fixed-point masses per 8-bit
+// digit at bits [shift, shift + 8) in the wave's LDS histogram (256 x 64-bit), then find the
+// largest digit d whose keys, together with the keys of larger digits, carry at least `need`.
+// Returns d and, via *above, the mass of the larger digits. All calls are wave-uniform, and
+// the histogram holds at least `need` in total.
+template <int S>
+__device__ __forceinline__ int radix_mass_digit(const uint32_t (&key)[S], const uint64_t (&u)[S],
+                                                uint32_t prefix, int shift, uint64_t need,
+                                                uint64_t* hist, int lane, uint64_t* above) {
+  *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+  *reinterpret_cast<u32x4*>(hist + 4 * lane + 2) = u32x4{0u, 0u, 0u, 0u};
+  __builtin_amdgcn_wave_barrier();
+  const int hs = shift + 8;
+#pragma unroll
+  for (int e = 0; e < S; ++e) {
+    const uint32_t k = key[e];
+    const bool in = k != 0u && u[e] != 0ull && (hs >= 32 || (k >> hs) == (prefix >> hs));
+    if (in) __hip_atomic_fetch_add(hist + ((k >> shift) & 0xffu), u[e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WAVEFRONT);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane l reads the four digits 4 (63 - l) .. 4 (63 - l) + 3, so lanes run from the highest
+  // digits down and an inclusive prefix sum over lanes gives the mass of digits >= 4 (63 - l)
+  const int g = 63 - lane;
+  const uint64_t b0 = hist[4 * g], b1 = hist[4 * g + 1], b2 = hist[4 * g + 2],
+                 b3 = hist[4 * g + 3];
+  const uint64_t t = b0 + b1 + b2 + b3;
+  const uint64_t suf = wave_prefix_sum_u64(t);
+  const uint64_t hi = suf - t;  // mass of the digits above 4 g + 3
+  const uint64_t m = ballot64(hi < need && suf >= need);
+  const int src = (int)__builtin_ctzll(m);  // exactly one lane holds the crossing digit
+  int d;
+  uint64_t a;
+  if (hi + b3 >= need) { d = 3; a = hi; }
+  else if (hi + b3 + b2 >= need) { d = 2; a = hi + b3; }
+  else if (hi + b3 + b2 + b1 >= need) { d = 1; a = hi + b3 + b2; }
+  else { d = 0; a = hi + b3 + b2 + b1; }
+  d = (int)lane_u32((uint32_t)(4 * g + d), src);
+  *above = ((uint64_t)lane_u32((uint32_t)(a >> 32), src) << 32) | lane_u32((uint32_t)a, src);
+  return d;
+}
+
 // Cumulative-mass selection of one row from its block probabilities p (slot e of lane l is key
-// block 64 e + l; entries past nkb are ignored); writes the kept bitmask words and count.
+// block 64 e + l; entries past nkb are ignored); writes the kept bitmask words and count. The
+// key T of the block that completes the prefix is found a byte at a time (radix_mass_digit),
+// starting below the high bytes every candidate key shares. `hist` is this wave's 256-entry
+// 64-bit LDS histogram.
 template <int S>
 __device__ __forceinline__ void select_mass_probs(const SelectArgs& a, const float (&prob)[S],
-                                                  int64_t row, int lane) {
+                                                  int64_t row, int lane, uint64_t* hist) {
   const int nkb = a.nkb;
   uint64_t u[S];
   uint32_t key[S];
@@ -401,23 +448,21 @@ __device__ __forceinline__ void select_mass_probs(const SelectArgs& a, const flo
   if (how == 2) {
     kmin = wave_min_dpp(kmin);
     kmax = wave_max_u32_dpp(kmax);
-    // invariant: the candidate keys >= T carry at least need_mass (T <= kmin at the start)
-    int bit = search_start(kmin, kmax, &T);
-    for (; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      uint64_t s = 0;
-#pragma unroll
-      for (int e = 0; e < S; ++e) s += key[e] >= cand ? u[e] : 0ull;
-      s = wave_total_u64(s);
-      if (s >= need_mass) T = cand;
+    // every candidate key shares the bits above the highest bit where kmin and kmax differ;
+    // the search starts at the byte holding that bit. `need` is the mass still to collect
+    // among the keys that match T's decided bytes.
+    uint64_t need = need_mass;
+    const int hb = search_start(kmin, kmax, &T);
+    for (int shift = hb < 0 ? -8 : (hb / 8) * 8; shift >= 0; shift -= 8) {
+      uint64_t ab;
+      const int d = radix_mass_digit<S>(key, u, T, shift, need, hist, lane, &ab);
+      T = (T & ~(0xffu << shift)) | ((uint32_t)d << shift);
+      need -= ab;
     }
-    uint64_t above = 0;
-#pragma unroll
-    for (int e = 0; e < S; ++e) above += key[e] > T ? u[e] : 0ull;
-    above = wave_total_u64(above);
-    // T is the key of a candidate whose mass completes the prefix, so uT > 0
+    // T is the key of a candidate whose mass completes the prefix, so uT > 0; the candidates
+    // above T carry need_mass - need
     const uint64_t uT = mass_units(key_to_float(T));
-    n_eq = (need_mass - above + uT - 1) / uT;
+    n_eq = (need + uT - 1) / uT;
   }
   uint32_t cnt = 0;
   uint64_t eq_seen = 0;
@@ -449,7 +494,7 @@ __device__ __forceinline__ void select_mass_probs(const SelectArgs& a, const flo
 // then the cumulative-mass selection.
 template <int S>
 __device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float* srow,
-                                                int64_t row, int lane) {
+                                                int64_t row, int lane, uint64_t* hist) {
   const int nkb = a.nkb;
   float val[S];
   float mx = -INFINITY;
@@ -474,7 +519,7 @@ __device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float
     val[e] *= inv;
     if (c < nkb && a.scores_out) a.scores_out[row * nkb + c] = val[e];
   }
-  select_mass_probs<S>(a, val, row, lane);
+  select_mass_probs<S>(a, val, row, lane, hist);
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin by id, so id b runs on XCD b % 8. Work item
@@ -490,8 +535,9 @@ __device__ __forceinline__ bool xcd_work_item(int64_t n_items, int64_t* item) {
 
 template <typename T, int D, int S, int MODE>
 __global__ __launch_bounds__(64 * kWaves) void score_select_kernel(SelectArgs a, int n_heads) {
-  // [kRowsPerWG][lds_stride] scores, then an 8 KiB area holding first the pooled queries
-  // (phases 0-1) and then one 256-bin histogram per wave (phase 2, Top-K)
+  // [kRowsPerWG][lds_stride] scores, then an area holding first the pooled queries (phases 0-1)
+  // and then one 256-bin histogram per wave (phase 2: 8 KiB of 32-bit counts in Top-K mode,
+  // 16 KiB of 64-bit masses in mass mode)
   extern __shared__ float s_lds[];
   const int tiles = (a.nqb + kRowsPerWG - 1) / kRowsPerWG;
   int64_t item;
@@ -516,7 +562,8 @@ __global__ __launch_bounds__(64 * kWaves) void score_select_kernel(SelectArgs a,
       select_topk_row<S>(a, srow, row, lane,
                          reinterpret_cast<uint32_t*>(s_lds + kRowsPerWG * a.lds_stride) + 256 * wave);
     else
-      select_mass_row<S>(a, srow, row, lane);
+      select_mass_row<S>(a, srow, row, lane,
+                         reinterpret_cast<uint64_t*>(s_lds + kRowsPerWG * a.lds_stride) + 256 * wave);
   }
 }
 
@@ -593,6 +640,7 @@ __global__ __launch_bounds__(256) void fill_csr_kernel(const uint64_t* __restric
 // row per wave, four rows per workgroup).
 template <int S>
 __global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const float* energy) {
+  __shared__ __attribute__((aligned(16))) uint64_t hist[4][256];
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.n_rows) return;
   const int lane = threadIdx.x & 63;
@@ -602,7 +650,7 @@ __global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const 
     const int c = e * 64 + lane;
     p[e] = c < a.nkb ? energy[row * a.nkb + c] : 0.f;
   }
-  select_mass_probs<S>(a, p, row, lane);
+  select_mass_probs<S>(a, p, row, lane, hist[threadIdx.x >> 6]);
 }
 
 hipError_t launch_exclusive_scan(const int32_t* counts, int32_t* out, int64_t n,
@@ -649,7 +697,9 @@ static hipError_t launch_score_select_dm(const SelectArgs& a, int64_t bh, hipStr
   const int64_t items = bh * ((a.nqb + kRowsPerWG - 1) / kRowsPerWG);
   const dim3 grid((unsigned)(8 * ((items + 7) / 8)));
   const dim3 block(64 * kWaves);
-  const size_t lds = (size_t)kRowsPerWG * a.lds_stride * sizeof(float) + 8192;
+  // the area after the scores holds the pooled queries (8 KiB at most), then one histogram per
+  // wave: 256 x 32-bit (Top-K) or 256 x 64-bit (mass)
+  const size_t lds = (size_t)kRowsPerWG * a.lds_stride * sizeof(float) + (MODE == 0 ? 8192 : 16384);
   const int slots = (a.nkb + 63) / 64;
 #define DBSP_SLOTS(N)                                                               \
   if (slots <= N) {                                                                 \
