@@ -568,28 +568,33 @@ __global__ __launch_bounds__(64 * kWaves) void score_select_kernel(SelectArgs a,
 }
 
 // Exclusive prefix sum of the per-row counts into row_ptr (one workgroup of 1024 threads).
-// Passes of 8192 rows: thread t takes rows 8 t .. 8 t + 7 of the pass (all loads issued first),
-// adds them, the 1024 thread totals are scanned (DPP wave scans, then the 16 wave totals), and
-// every thread writes its 8 exclusive prefixes. Counts are small (at most 2048 per row), so
-// int32 prefixes suffice: the host rejects an nnz bound above INT32_MAX.
+// Passes of 1024 kPer rows: thread t takes rows kPer t .. kPer t + kPer - 1 of the pass (all
+// loads issued first, 16 bytes at a time), adds them, the 1024 thread totals are scanned (DPP
+// wave scans, then the 16 wave totals), and every thread writes its kPer exclusive prefixes
+// (16 bytes at a time when row_ptr allows). The launch picks kPer so that most row counts take
+// one pass. Counts are small (at most 2048 per row), so int32 prefixes suffice: the host rejects
+// an nnz bound above INT32_MAX.
+template <int kPer>
 __global__ __launch_bounds__(1024) void scan_counts_kernel(const int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ row_ptr,
                                                            int64_t rows) {
-  constexpr int kPer = 8;
+  static_assert(kPer % 4 == 0, "whole 16-byte groups");
   constexpr int64_t kPass = 1024 * kPer;
   __shared__ uint32_t wave_tot[16];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
+  const bool vec_out = (reinterpret_cast<uintptr_t>(row_ptr) & 15u) == 0;
   uint32_t carry = 0;  // sum of all earlier passes
   for (int64_t base = 0; base < rows; base += kPass) {
     const int64_t r0 = base + (int64_t)t * kPer;
+    const bool whole = r0 + kPer <= rows;
     int32_t c[kPer];
-    if (r0 + kPer <= rows) {  // 32 contiguous bytes per thread (counts is 256-byte aligned)
-      const u32x4 a = load_u32x4(counts + r0), b = load_u32x4(counts + r0 + 4);
+    if (whole) {  // kPer * 4 contiguous bytes per thread (counts is 256-byte aligned)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = (int32_t)a[i];
-        c[4 + i] = (int32_t)b[i];
+      for (int g = 0; g < kPer / 4; ++g) {
+        const u32x4 a = load_u32x4(counts + r0 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[4 * g + i] = (int32_t)a[i];
       }
     } else {
 #pragma unroll
@@ -606,10 +611,23 @@ __global__ __launch_bounds__(1024) void scan_counts_kernel(const int32_t* __rest
     uint32_t pass_total = 0;
     for (int i = 0; i < 16; ++i) pass_total += wave_tot[i];
     uint32_t run = before + incl - own;  // exclusive prefix of this thread's first row
+    if (whole && vec_out) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (r0 + i < rows) row_ptr[r0 + i] = (int32_t)run;
-      run += (uint32_t)c[i];
+      for (int g = 0; g < kPer / 4; ++g) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = run;
+          run += (uint32_t)c[4 * g + i];
+        }
+        *reinterpret_cast<u32x4*>(row_ptr + r0 + 4 * g) = o;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (r0 + i < rows) row_ptr[r0 + i] = (int32_t)run;
+        run += (uint32_t)c[i];
+      }
     }
     carry += pass_total;
     __syncthreads();  // wave_tot is rewritten by the next pass
@@ -655,7 +673,12 @@ __global__ __launch_bounds__(256) void select_energy_kernel(SelectArgs a, const 
 
 hipError_t launch_exclusive_scan(const int32_t* counts, int32_t* out, int64_t n,
                                  hipStream_t stream) {
-  scan_counts_kernel<<<1, 1024, 0, stream>>>(counts, out, n);
+  if (n <= 1024 * 8)
+    scan_counts_kernel<8><<<1, 1024, 0, stream>>>(counts, out, n);
+  else if (n <= 1024 * 16)
+    scan_counts_kernel<16><<<1, 1024, 0, stream>>>(counts, out, n);
+  else
+    scan_counts_kernel<32><<<1, 1024, 0, stream>>>(counts, out, n);
   return hipGetLastError();
 }
 
