@@ -645,8 +645,11 @@ __global__ __launch_bounds__(256) void fill_csr_kernel(const uint64_t* __restric
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
   int64_t out = row_ptr[row];
+  // the row's words in one load (lane e holds word e; words <= 32), then read back per word
+  const uint64_t mine = lane < words ? masks[row * words + lane] : 0ull;
   for (int e = 0; e < words; ++e) {
-    const uint64_t w = masks[row * words + e];
+    const uint64_t w = ((uint64_t)__builtin_amdgcn_readlane((int)(mine >> 32), e) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, e);
     const bool keep = (w >> lane) & 1ull;
     const int64_t pos = out + mbcnt64(w);
     if (keep && pos < col_capacity) col_idx[pos] = e * 64 + lane;
