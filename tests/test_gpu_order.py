@@ -117,3 +117,39 @@ def test_outputs_on_the_host_are_rejected():
     with pytest.raises(ValueError):
         m.lpt_order(q, k, idx, out=torch.empty(w.rows, dtype=torch.int32))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("nkb", [37, 8200])
+def test_lpt_order_from_a_given_csr(nkb):
+    # the order depends only on the CSR row lengths, so a synthetic CSR drives both sort paths:
+    # buckets in LDS per head (up to 8,191 key blocks) and the global-bucket launches beyond
+    import ctypes
+    from dynamic_block_sparse_pool_amd import _abi
+    lib = _abi.load()
+    batch, heads, nqb = 2, 3, 300
+    rows = batch * heads * nqb
+    rng = np.random.default_rng(nkb)
+    lens = rng.integers(0, nkb + 1, size=rows)
+    lens[rng.random(rows) < 0.2] = nkb                     # some rows keep every block
+    lens[rng.random(rows) < 0.1] = 0                       # and some none
+    rp = np.zeros(rows + 1, np.int64)
+    np.cumsum(lens, out=rp[1:])
+    say(f"case synthetic CSR: nkb={nkb} rows={rows} nnz={int(rp[-1])}")
+    row_ptr = torch.from_numpy(rp.astype(np.int32)).cuda()
+    dims = _abi.Dims(batch, heads, nqb * BLOCK, nkb * BLOCK, 128, _abi.DBSP_BF16)
+    need = ctypes.c_uint64()
+    assert lib.dbsp_row_order_workspace_bytes(ctypes.byref(dims), ctypes.byref(need)) == 0
+    ws = torch.empty(max(need.value, 1), dtype=torch.uint8, device="cuda")
+    order = torch.empty(rows, dtype=torch.int32, device="cuda")
+    st = lib.dbsp_row_order_lpt(ctypes.c_void_p(row_ptr.data_ptr()), ctypes.byref(dims),
+                                int(rp[-1]), ctypes.c_void_p(order.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    o = order.cpu().numpy()
+    assert np.array_equal(np.sort(o), np.arange(rows))      # a permutation
+    head = o // nqb
+    assert np.array_equal(head, np.repeat(np.arange(batch * heads), nqb))   # heads in order
+    for hh in range(batch * heads):
+        assert (np.diff(lens[o[head == hh]]) <= 0).all()    # longest first per head
