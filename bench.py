@@ -8,29 +8,35 @@ Default workload: the 720p final scale (32 heads, d = 128, bf16, Lq = 72,192 que
 Lk = 144,896 keys = 512 text + 72,192 reference + 72,192 current tokens, text forced, Top-K
 density 0.09375). Prints one JSON line.
 
-Reported numbers:
-  value           executed attention FLOP of the step / step time (TFLOP/s)
-  select_ms       per-step time of the selection kernels (HIP events on the launch stream), mean
-                  of the timed steps; select_ms_p10/p50/p90 give the spread. In mass mode it
-                  includes the longest-first row order that the attention launch then follows
-                  (--row-order)
-  select_GBps     selection's algorithmic bytes (Q + K read once, CSR written) / select_ms
-  attn_ms         per-step time of the attention kernel (HIP events on the launch stream), mean;
-                  attn_ms_p10/p50/p90 give the spread
-  attn_kv_GBps    attention's algorithmic bytes (Q and O once, K and V of every kept block once
-                  per query block) / attn_ms, and attn_kv_hbm_frac against 8 TB/s: the executed
-                  FLOP per such byte is 2 x 128 = 256 / 2 = 128 for 128-token blocks, below the
-                  chip's FLOP-per-byte ridge, so without reuse across query blocks in the caches
-                  the HBM side bounds the kernel before the MFMA side does
-  cold            the same two calls timed after overwriting a 512 MiB scratch buffer before
-                  every iteration (outside the timed region), which evicts the 256 MiB
-                  last-level cache: medians over the cold iterations
-  copy_GBps       a plain device-to-device copy of 1 GiB (read + write bytes / time) as the
-                  achievable HBM ceiling, with select_copy_frac = select_GBps / copy_GBps
-  roofline        the attention kernel (dominant): executed FLOP / its average launch time,
-                  against the bf16 dense MFMA peak; traffic = its HBM bytes per launch from the
-                  committed FETCH_SIZE / WRITE_SIZE counter summary, when that summary was
-                  taken on the current kernel source (else null)
+Reported numbers (the measurement protocol: HIP events on the launch stream; the headline
+kernel times are medians over iterations that each start with the 256 MiB last-level cache
+flushed; warm figures are labelled *_warm):
+  value           executed attention FLOP of the step / step time (TFLOP/s), over the K timed
+                  back-to-back steps (ms_per_step)
+  select_ms       selection kernels (pool Q and K, score, select, CSR; in mass mode also the
+                  longest-first row order the attention launch then follows, --row-order),
+                  timed alone after a cache flush: median of --cold-iters iterations, with
+                  select_ms_p10 / _p90; select_ms_warm is the mean over the timed steps
+  select_GBps     selection's algorithmic bytes (Q + K read once, CSR written) / select_ms, and
+                  select_hbm_frac against 8 TB/s
+  attn_ms         the attention kernel timed alone after a cache flush: median (p10 / p90
+                  beside it); attn_ms_warm is the mean over the timed steps
+  attn_TFLOPs     executed attention FLOP / attn_ms, and attn_mfma_frac against the bf16 dense
+                  peak
+  attn_kv_gathered_GBps
+                  K and V bytes of every kept (row, key block) pair plus Q and O once, per
+                  second of attn_ms: the bytes the kernel gathers into LDS, most of them served
+                  by the caches (not an HBM figure)
+  copy_GBps       a plain device-to-device copy of 1 GiB (read + write bytes / time) and
+  read_GBps       a read-only streaming pass over 1 GiB (bytes read / time; the probe kernel of
+                  libdbsp_probe.so): achievable HBM ceilings
+                  measured on the same GPU, with select_copy_frac and select_read_frac
+  roofline        the attention kernel (dominant): executed FLOP / its mean launch time over the
+                  timed steps, against the bf16 dense MFMA peak; traffic = its L2-miss bytes per
+                  launch (FETCH_SIZE and WRITE_SIZE counters, scaled by a copy calibration) from
+                  the committed counter summary when that summary was taken on the current
+                  kernel source (else null). Those bytes leave the L2 for the fabric; part of
+                  them is served by the last-level cache rather than HBM
   gemm_ceiling    context for the MFMA fraction, measured after the timed region: a dense
                   bf16 16384^3 GEMM through torch.matmul (the vendor's hipBLASLt) on the same
                   GPU, its TFLOP/s, fraction of the nominal peak, and attention's throughput as
@@ -89,8 +95,8 @@ def parse():
                          "and timed with it) or row order; auto = lpt in mass mode")
     ap.add_argument("--only-copy", action="store_true",
                     help="run only the 1 GiB device copy (counter calibration) and exit")
-    ap.add_argument("--cold-iters", type=int, default=8,
-                    help="iterations of the cache-flushed timing pass (0 skips it)")
+    ap.add_argument("--cold-iters", type=int, default=20,
+                    help="iterations of the cache-flushed timing of each kernel (at least 1)")
     return ap.parse_args()
 
 
@@ -140,6 +146,42 @@ def copy_ceiling(torch, dev, reps: int = 5) -> float:
     ms = e0.elapsed_time(e1) / reps
     del src, dst
     return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def read_ceiling(torch, dev, reps: int = 5):
+    """Bytes read / time of a read-only pass over 1 GiB by the read-bandwidth probe
+    (libdbsp_probe.so: 16-byte non-temporal loads, one word written per workgroup), the best of
+    a few launch sizes: the HBM read ceiling a streaming kernel reaches on this GPU. None when
+    the probe library is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "dynamic_block_sparse_pool_amd", "libdbsp_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dbsp_probe_read.restype = ctypes.c_int32
+    lib.dbsp_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                    ctypes.c_int32, ctypes.c_void_p]
+    n = 1 << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    out = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    best = 0.0
+    for grid in (2048, 4096, 8192, 16384):
+        run = lambda: lib.dbsp_probe_read(ctypes.c_void_p(x.data_ptr()), n,
+                                          ctypes.c_void_p(out.data_ptr()), grid, stream)
+        if run() != 0:
+            return None
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        best = max(best, n / (ms * 1e-3) / 1e9)
+    del x, out
+    return best
 
 
 def cpu_baseline(w, q, k, v, row_ptr, col_idx, nnz, flop_per_pair, budget_s):
@@ -526,27 +568,35 @@ def main():
 
     sel_list = [e[0].elapsed_time(e[1]) for e in ev]
     att_list = [e[1].elapsed_time(e[2]) for e in ev]
-    sel_ms = sum(sel_list) / n_ev
-    att_ms = sum(att_list) / n_ev
+    sel_warm = sum(sel_list) / n_ev
+    att_warm = sum(att_list) / n_ev
     ms_per_step = wall * 1e3 / args.steps
 
-    # cold pass: evict the last-level cache before every iteration, outside the timed region
-    cold = None
-    if args.cold_iters > 0:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cs, ca = [], []
-        for it in range(args.cold_iters):
-            scratch.fill_(it & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(e)
-            torch.cuda.synchronize()
-            cs.append(e[0].elapsed_time(e[1]))
-            ca.append(e[1].elapsed_time(e[2]))
-        del scratch
-        cold = {"iters": args.cold_iters, "flush_bytes": 512 << 20,
-                "select_ms_p50": round(percentiles(cs)[1], 4),
-                "attn_ms_p50": round(percentiles(ca)[1], 4)}
+    # the protocol's headline times: each kernel alone, after overwriting a 512 MiB scratch
+    # buffer (outside the timed region) so that the 256 MiB last-level cache holds none of its
+    # inputs; medians over the iterations
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cs, ca = [], []
+    for it in range(max(args.cold_iters, 1)):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        scratch.fill_(it & 0xFF)
+        e[0].record(stream)
+        plan.run(q, k)
+        if lpt:
+            dbsp.lpt_order(q, k, idx, out=order, workspace=order_ws)
+        e[1].record(stream)
+        scratch.fill_((it + 128) & 0xFF)
+        e[2].record(stream)
+        dbsp.sparse_attn_fwd(q, k, v, idx, out=out, row_order=order)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        cs.append(e[0].elapsed_time(e[1]))
+        ca.append(e[2].elapsed_time(e[3]))
+    del scratch
+    sp, ap_ = percentiles(cs), percentiles(ca)
+    sel_ms, att_ms = sp[1], ap_[1]
     copy_gbps = copy_ceiling(torch, dev)
+    read_gbps = read_ceiling(torch, dev)
 
     nnz = idx.nnz()
     rows = w.rows
@@ -555,14 +605,12 @@ def main():
     elt = 2 if w.dtype == "bf16" else 4
     sel_bytes = (w.batch * w.heads * (w.lq + w.lk) * w.head_dim * elt) + 4 * (rows + 1) + 4 * nnz
     att_tflops = exec_flop / (att_ms * 1e-3) / 1e12
+    att_tflops_warm = exec_flop / (att_warm * 1e-3) / 1e12
     sel_gbps = sel_bytes / (sel_ms * 1e-3) / 1e9
     tok_bytes = 128 * w.head_dim * elt  # one block of K or V
     att_bytes = nnz * 2 * tok_bytes + 2 * w.batch * w.heads * w.lq * w.head_dim * elt
     att_gbps = att_bytes / (att_ms * 1e-3) / 1e9
-    if cold is not None:
-        cold["select_GBps"] = round(sel_bytes / (cold["select_ms_p50"] * 1e-3) / 1e9, 1)
-        cold["attn_TFLOPs"] = round(exec_flop / (cold["attn_ms_p50"] * 1e-3) / 1e12, 2)
-    sp, ap_ = percentiles(sel_list), percentiles(att_list)
+    sw, aw = percentiles(sel_list), percentiles(att_list)
     traffic = stored_traffic(w.name)
     res = {
         "metric": METRIC,
@@ -584,28 +632,36 @@ def main():
             "nnz": nnz, "executed_density": round(nnz / (rows * w.n_k_blocks), 5),
             "output_dtype": "bf16" if bf16 else "f32", "row_order": "lpt" if lpt else "row",
         },
+        "timing": f"select_ms / attn_ms: each kernel alone after a 512 MiB cache flush, median "
+                  f"of {len(cs)}; *_warm: the {n_ev} back-to-back timed steps",
         "select_ms": round(sel_ms, 4),
-        "select_ms_p10": round(sp[0], 4), "select_ms_p50": round(sp[1], 4),
-        "select_ms_p90": round(sp[2], 4),
+        "select_ms_p10": round(sp[0], 4), "select_ms_p90": round(sp[2], 4),
         "select_GBps": round(sel_gbps, 1),
         "select_hbm_frac": round(sel_gbps / PEAK_HBM_GBPS, 4),
+        "select_ms_warm": round(sel_warm, 4), "select_ms_warm_p50": round(sw[1], 4),
+        "select_hbm_frac_warm": round(sel_bytes / (sel_warm * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "copy_GBps": round(copy_gbps, 1),
+        "read_GBps": round(read_gbps, 1) if read_gbps else None,
         "select_copy_frac": round(sel_gbps / copy_gbps, 4),
+        "select_read_frac": round(sel_gbps / read_gbps, 4) if read_gbps else None,
         "attn_ms": round(att_ms, 4),
-        "attn_ms_p10": round(ap_[0], 4), "attn_ms_p50": round(ap_[1], 4),
-        "attn_ms_p90": round(ap_[2], 4),
+        "attn_ms_p10": round(ap_[0], 4), "attn_ms_p90": round(ap_[2], 4),
         "attn_TFLOPs": round(att_tflops, 2),
         "attn_mfma_frac": round(att_tflops / PEAK_BF16_TFLOPS, 4) if bf16 else None,
-        "attn_kv_GBps": round(att_gbps, 1),
-        "attn_kv_hbm_frac": round(att_gbps / PEAK_HBM_GBPS, 4),
-        "cold": cold,
-        "roofline": ({"bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                      "unit": "TFLOP/s", "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_ms_warm": round(att_warm, 4), "attn_ms_warm_p50": round(aw[1], 4),
+        "attn_mfma_frac_warm": round(att_tflops_warm / PEAK_BF16_TFLOPS, 4) if bf16 else None,
+        "attn_kv_gathered_GBps": round(att_gbps, 1),
+        "roofline": ({"bound": "mfma", "achieved": round(att_tflops_warm, 2),
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(att_tflops_warm / PEAK_BF16_TFLOPS, 4),
                       "traffic": traffic, "kernel": "attn_fwd_bf16_kernel",
-                      "per_launch_flop": exec_flop} if bf16 else
-                     {"bound": "alu", "achieved": round(att_tflops, 4),
+                      "per_launch_flop": exec_flop,
+                      "traffic_what": "L2-miss bytes per launch (FETCH_SIZE and WRITE_SIZE, "
+                                      "copy-calibrated); part is served by the last-level cache"}
+                     if bf16 else
+                     {"bound": "alu", "achieved": round(att_tflops_warm, 4),
                       "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
-                      "frac": round(att_tflops / PEAK_F32_VALU_TFLOPS, 6), "traffic": None,
+                      "frac": round(att_tflops_warm / PEAK_F32_VALU_TFLOPS, 6), "traffic": None,
                       "kernel": "attn_fwd_f32_kernel", "per_launch_flop": exec_flop}),
     }
     if bf16 and not args.no_ceiling:

@@ -3,7 +3,8 @@
     python -m dynamic_block_sparse_pool_amd.build [--verbose] [--save-temps DIR]
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel), then linked into
-dynamic_block_sparse_pool_amd/libdbsp.so next to this file.
+dynamic_block_sparse_pool_amd/libdbsp.so next to this file. The benchmark's read-bandwidth
+probe (csrc/probe/) is built into its own libdbsp_probe.so beside it.
 """
 from __future__ import annotations
 
@@ -17,6 +18,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libdbsp.so")
+PROBE_PATH = os.path.join(PKG_DIR, "libdbsp_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
@@ -70,7 +72,23 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
+    build_probe(verbose)
     return LIB_PATH
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's read-bandwidth probe, a separate small library."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if p.returncode != 0:
+        print(p.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for the read-bandwidth probe")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
 
 
 def main(argv=None):

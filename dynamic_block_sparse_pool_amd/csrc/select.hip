@@ -390,7 +390,9 @@ __device__ __forceinline__ int radix_mass_digit(const uint32_t (&key)[S], const 
   const uint64_t suf = wave_prefix_sum_u64(t);
   const uint64_t hi = suf - t;  // mass of the digits above 4 g + 3
   const uint64_t m = ballot64(hi < need && suf >= need);
-  const int src = (int)__builtin_ctzll(m);  // exactly one lane holds the crossing digit
+  // exactly one lane holds the crossing digit when the histogram holds `need`; an empty ballot
+  // (only possible for rows outside the documented input range) falls back to lane 0
+  const int src = m ? (int)__builtin_ctzll(m) : 0;
   int d;
   uint64_t a;
   if (hi + b3 >= need) { d = 3; a = hi; }
@@ -460,9 +462,10 @@ __device__ __forceinline__ void select_mass_probs(const SelectArgs& a, const flo
       need -= ab;
     }
     // T is the key of a candidate whose mass completes the prefix, so uT > 0; the candidates
-    // above T carry need_mass - need
+    // above T carry need_mass - need. (uT == 0 only for rows outside the documented range,
+    // whose 64-bit sums wrapped: such a row keeps no block equal to T instead of dividing by 0.)
     const uint64_t uT = mass_units(key_to_float(T));
-    n_eq = (need + uT - 1) / uT;
+    n_eq = uT ? (need + uT - 1) / uT : 0;
   }
   uint32_t cnt = 0;
   uint64_t eq_seen = 0;

@@ -28,7 +28,10 @@ __device__ __forceinline__ void row_extent(const int32_t* row_ptr, int64_t row, 
 }
 
 // Entry e of a row starts (ends) a run: in range, and the entry before (after) it is not the
-// block just below (above).
+// in-range block just below (above). The neighbour has to be in range itself: an out-of-range
+// -1 before block 0 (or nkb after block nkb - 1) continues nothing, so every chain of in-range
+// entries that step by +1 has exactly one start (its first entry) and one stop (its last), and
+// the k-th start and the k-th stop of a row always belong to the same run.
 __device__ __forceinline__ void run_flags(const int32_t* col_idx, int64_t e, int64_t beg,
                                           int64_t end, int nkb, bool* start, bool* stop,
                                           int* c_out) {
@@ -37,8 +40,8 @@ __device__ __forceinline__ void run_flags(const int32_t* col_idx, int64_t e, int
   const bool in = live && c >= 0 && c < nkb;
   const int prev = (live && e > beg) ? col_idx[e - 1] : -2;
   const int next = (live && e + 1 < end) ? col_idx[e + 1] : -2;
-  *start = in && prev != c - 1;
-  *stop = in && next != c + 1;
+  *start = in && !(c > 0 && prev == c - 1);
+  *stop = in && !(c + 1 < nkb && next == c + 1);
   *c_out = c;
 }
 

@@ -322,7 +322,10 @@ int32_t dbsp_retained_mass(const float* energy, const dbsp_dims* dims, const int
  * energies of dbsp_block_energy, instead of the pooled-score softmax. Step 4b of
  * dbsp_sparse_select with p_ic = energy[r][c] (fixed-point masses floor(p * 2^62), forced
  * blocks first, ties to the lower index, keep all if the row never reaches tau, tau = 1 keeps
- * all); step 5 for the output. energy: device float32 [rows, lk / 128], values in [0, 1].
+ * all); step 5 for the output. energy: device float32 [rows, lk / 128], values in [0, 1]
+ * and each row summing to at most 2 (any row of probabilities, rounding included, does: the
+ * fixed-point row sums are then below 2^63 and exact in 64 bits; rows above that bound are not
+ * checked and give an unspecified mask, never an access outside the buffers).
  * workspace: at least dbsp_select_energy_workspace_bytes bytes of device memory, 256-byte
  * aligned. The nnz bound is rows * (lk / 128) (dbsp_select_nnz_bound in DBSP_MASS mode).
  * Errors: as dbsp_sparse_select (ranges, tau in (0, 1], capacity, workspace); DBSP_ERR_UNSUPPORTED

@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
 Every mask row is checked bit-exact against the oracle selecting from the GPU's own scores.
-Pooled scores are checked against the oracle's pooling on sampled heads; attention outputs on
-sampled rows (first, last, and seeded random rows), each computed by the oracle one by one.
+Pooled scores are checked against the oracle's pooling on sampled heads; attention outputs and
+lse on every row of one whole head (all its query blocks, each computed by the oracle one by
+one) and on sampled rows of the other heads (first, last, and seeded random rows).
 """
 import math
 
@@ -34,7 +35,7 @@ def test_full_size(name):
     kw = dict(density=w.param) if w.mode == "topk" else dict(mass=w.param)
     plan = dbsp.SelectPlan(q, k, w.text, w.extra, return_scores=True, **kw)
     idx = plan.run(q, k)
-    o = dbsp.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32)
+    o, lse = dbsp.sparse_attn_fwd(q, k, v, idx, out_dtype=torch.float32, return_lse=True)
     # the bf16 output the benchmark times, in its launch order (longest rows first per head in
     # mass mode)
     order = dbsp.lpt_order(q, k, idx) if w.mode == "mass" else None
@@ -88,3 +89,17 @@ def test_full_size(name):
         o16_g = P.host(o16[b, h, i * P.BLOCK:(i + 1) * P.BLOCK])
         assert np.array_equal(o16_g, P.host(torch.from_numpy(o_g.astype(np.float32)).to(torch.bfloat16)))
     say(f"  attention rows {rows}: worst max err {worst:.2e}")
+
+    # one whole head end to end: every query block of head H / 2 (batch 0) against the oracle
+    hw = w.heads // 2
+    qh, kh, vh = head_host(q, 0, hw), head_host(k, 0, hw), head_host(v, 0, hw)
+    r0 = hw * nqb
+    rp_h = rp[r0:r0 + nqb + 1] - rp[r0]
+    ci_h = ci[rp[r0]:rp[r0 + nqb]]
+    o_ref, lse_ref = oracle.attention_rows(qh, kh, vh, rp_h, ci_h, scale=scale)
+    o_ref, lse_ref = P.rows_to_tokens(o_ref, lse_ref, 1, 1, w.lq)
+    mx, mean = P.check_attention(P.host(o[0:1, hw:hw + 1]), P.host(lse[0:1, hw:hw + 1]), o_ref,
+                                 lse_ref, w.dtype == "bf16")
+    o16_h = P.host(o16[0:1, hw:hw + 1])
+    assert np.array_equal(o16_h, P.host(o[0:1, hw:hw + 1].to(torch.bfloat16)))
+    say(f"  head {hw}: all {nqb} query blocks, O max err {mx:.2e} mean {mean:.2e}")

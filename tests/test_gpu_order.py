@@ -119,14 +119,17 @@ def test_outputs_on_the_host_are_rejected():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("nkb", [37, 8200])
-def test_lpt_order_from_a_given_csr(nkb):
+@pytest.mark.parametrize("nkb,nqb", [(37, 300), (1500, 1100), (8191, 64), (8200, 300)])
+def test_lpt_order_from_a_given_csr(nkb, nqb):
     # the order depends only on the CSR row lengths, so a synthetic CSR drives both sort paths:
-    # buckets in LDS per head (up to 8,191 key blocks) and the global-bucket launches beyond
+    # buckets in LDS per head (up to 8,191 key blocks: one bucket per thread and a single pass
+    # over the rows at 37 x 300; several buckets per thread and several passes over the rows at
+    # 1,500 x 1,100 (the 720p final scale under a longest-first order has 1,132 key blocks); the
+    # largest LDS bucket array at 8,191) and the global-bucket launches beyond
     import ctypes
     from dynamic_block_sparse_pool_amd import _abi
     lib = _abi.load()
-    batch, heads, nqb = 2, 3, 300
+    batch, heads = 2, 3
     rows = batch * heads * nqb
     rng = np.random.default_rng(nkb)
     lens = rng.integers(0, nkb + 1, size=rows)

@@ -28,13 +28,13 @@ def say(msg):
     print(f"[gpu-parity] {msg}", flush=True)
 
 
-def run_path(w: Workload, q, k, v, out_dtype=torch.float32, **kw):
+def run_path(w: Workload, q, k, v, out_dtype=torch.float32, out=None, **kw):
     m = dbsp()
     if w.mode == "topk":
         idx = m.sparse_select(q, k, w.text, w.extra, density=w.param, return_scores=True, **kw)
     else:
         idx = m.sparse_select(q, k, w.text, w.extra, mass=w.param, return_scores=True, **kw)
-    o, lse = m.sparse_attn_fwd(q, k, v, idx, out_dtype=out_dtype, return_lse=True)
+    o, lse = m.sparse_attn_fwd(q, k, v, idx, out_dtype=out_dtype, return_lse=True, out=out)
     torch.cuda.synchronize()
     return idx, o, lse
 
@@ -47,12 +47,15 @@ def oracle_select_on(w: Workload, scores2d: np.ndarray, forced: np.ndarray, topk
     return oracle.select_mass(scores2d, forced, w.param)
 
 
-def full_check_small(w: Workload, seed=3, inputs=None, score_scale=None):
+def full_check_small(w: Workload, seed=3, inputs=None, score_scale=None, out=None):
+    """Selection and attention of workload w through the C ABI against the oracle on the same
+    values: every score, every mask row and CSR entry, every output and lse. `inputs` may be
+    strided views and `out` a strided fp32 output view (the oracle reads their values)."""
     say(f"case {w.name} B={w.batch} H={w.heads} Lq={w.lq} Lk={w.lk} d={w.head_dim} {w.dtype} "
         f"{w.mode}={w.param} seed={seed}")
     q, k, v = inputs if inputs is not None else make_qkv(w, device="cuda", seed=seed)
     kw = {} if score_scale is None else {"score_scale": score_scale}
-    idx, o, lse = run_path(w, q, k, v, **kw)
+    idx, o, lse = run_path(w, q, k, v, out=out, **kw)
     qh, kh, vh = P.host(q), P.host(k), P.host(v)
     ref = oracle.sparse_select(qh, kh, w.text, w.extra, w.mode, w.param, score_scale=score_scale)
     nkb, nqb = w.n_k_blocks, w.n_q_blocks

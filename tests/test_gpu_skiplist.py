@@ -65,3 +65,44 @@ def test_intervals_random_and_extreme_masks():
     idx = m.BlockIndex(torch.from_numpy(rp.astype(np.int32)).cuda(),
                        torch.from_numpy(ci.astype(np.int32)).cuda(), nqb, nkb, None)
     check_round_trip(idx, kept, batch, heads, nqb, nkb)
+
+
+def test_intervals_skip_out_of_range_neighbours():
+    # rows of an ascending CSR that also hold out-of-range entries next to the range ends: a -1
+    # right before block 0 and nkb right after block nkb - 1 must neither join nor split a run,
+    # so the encoding equals the oracle's encoding of the in-range mask (the kernels skip
+    # out-of-range entries)
+    nkb = 11
+    rows_cols = [
+        [-1, 0, 1, 2, 6, nkb - 1, nkb],
+        [-5, -1, 0],
+        [nkb - 1, nkb, nkb + 3],
+        [-1],
+        [nkb],
+        [-1, 0, nkb - 2, nkb - 1, nkb],
+        [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11],
+        [],
+    ]
+    batch, heads, nqb = 1, 1, len(rows_cols)
+    rp = np.zeros(nqb + 1, np.int64)
+    np.cumsum([len(r) for r in rows_cols], out=rp[1:])
+    ci = np.array([c for r in rows_cols for c in r], np.int64)
+    kept = np.zeros((nqb, nkb), bool)
+    for r, cols in enumerate(rows_cols):
+        for c in cols:
+            if 0 <= c < nkb:
+                kept[r, c] = True
+    say(f"case out-of-range neighbours: rows={nqb} nkb={nkb} entries={ci.size}")
+    m = dbsp()
+    idx = m.BlockIndex(torch.from_numpy(rp.astype(np.int32)).cuda(),
+                       torch.from_numpy(ci.astype(np.int32)).cuda(), nqb, nkb, None)
+    iv_ptr, iv = m.to_intervals(idx, batch, heads)
+    back = m.from_intervals(iv_ptr, iv, nqb, nkb, batch, heads)
+    torch.cuda.synchronize()
+    ptr_ref, iv_ref = oracle.to_intervals(kept)
+    ptr = iv_ptr.cpu().numpy().astype(np.int64)
+    np.testing.assert_array_equal(ptr, ptr_ref)
+    np.testing.assert_array_equal(iv.cpu().numpy()[:ptr[-1]].astype(np.int64), iv_ref)
+    brp = back.row_ptr.cpu().numpy().astype(np.int64)
+    bci = back.col_idx.cpu().numpy().astype(np.int64)
+    np.testing.assert_array_equal(P.csr_to_kept(brp, bci, nkb), kept)

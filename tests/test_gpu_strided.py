@@ -1,14 +1,17 @@
 """Strided Q / K / V / O views: a [batch, L, heads, head_dim] layout seen head-major, keys and
-values shared by all heads (head stride 0), and a strided output. The same values in a
-different layout must give bit-identical CSRs and outputs to the contiguous call (the kernels
-read the same numbers in the same order), which also ties them to the oracle through the
-contiguous parity tests."""
+values shared by all heads (head stride 0), and a strided output.
+
+Each strided call is checked against the oracle on the values it reads, with the parity bars of
+the contiguous path: pooled scores, every mask row and CSR entry, every output and lse. The
+same values in the contiguous layout must also give bit-identical results (the kernels read the
+same numbers in the same order)."""
 import numpy as np
 import pytest
 import torch
 
 from synth import BLOCK, WORKLOADS, make_qkv, small_variants
 from tests import parity as P
+from tests.test_gpu_parity import full_check_small
 
 pytestmark = pytest.mark.gpu
 
@@ -44,17 +47,25 @@ CASES = {
 }
 
 
+def bshd_out(w):
+    return torch.empty((w.batch, w.lq, w.heads, w.head_dim), dtype=torch.float32,
+                       device="cuda").transpose(1, 2)
+
+
 @pytest.mark.parametrize("name", list(CASES))
-def test_bshd_views_match_contiguous(name):
+def test_bshd_views_against_oracle(name):
     w = CASES[name]
     say(f"case {name}: B={w.batch} H={w.heads} Lq={w.lq} Lk={w.lk} {w.dtype}")
     q, k, v = make_qkv(w, device="cuda", seed=71)
-    idx_c, o_c, l_c = run(q, k, v, w)
     qv, kv, vv = bshd_view(q), bshd_view(k), bshd_view(v)
     assert not qv.is_contiguous() and torch.equal(qv, q)
-    out_v = torch.empty((w.batch, w.lq, w.heads, w.head_dim), dtype=torch.float32,
-                        device="cuda").transpose(1, 2)
-    idx_s, o_s, l_s = run(qv, kv, vv, w, out=out_v)
+    out_v = bshd_out(w)
+    assert not out_v.is_contiguous()
+    # the strided selection and attention (strided output too) against the oracle
+    idx_s, o_s, l_s = full_check_small(w, inputs=(qv, kv, vv), out=out_v)
+    assert o_s.data_ptr() == out_v.data_ptr()
+    # and bit-identical to the contiguous call on the same values
+    idx_c, o_c, l_c = run(q, k, v, w)
     n = idx_c.nnz()
     assert n == idx_s.nnz()
     assert torch.equal(idx_c.row_ptr, idx_s.row_ptr)
@@ -63,15 +74,15 @@ def test_bshd_views_match_contiguous(name):
     assert torch.equal(o_c, o_s) and torch.equal(l_c, l_s)
 
 
-def test_keys_shared_across_heads():
+def test_keys_shared_across_heads_against_oracle():
     # multi-query style: one K and V per batch entry read by every head through a 0 head stride
     w = small_variants()["final_small"].with_(heads=3)
     say("case shared K / V (head stride 0)")
     q, k, v = make_qkv(w, device="cuda", seed=72)
     k1, v1 = k[:, :1].expand(-1, w.heads, -1, -1), v[:, :1].expand(-1, w.heads, -1, -1)
     assert k1.stride(1) == 0
+    idx_s, o_s, l_s = full_check_small(w, inputs=(q, k1, v1))
     idx_c, o_c, l_c = run(q, k1.contiguous(), v1.contiguous(), w)
-    idx_s, o_s, l_s = run(q, k1, v1, w)
     n = idx_c.nnz()
     assert torch.equal(idx_c.col_idx[:n], idx_s.col_idx[:n])
     assert torch.equal(o_c, o_s) and torch.equal(l_c, l_s)
