@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libdbsp.so")
 
 DBSP_BLOCK = 128
 DBSP_MAX_KEY_BLOCKS = 2048
+DBSP_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 DBSP_OK = 0
 DBSP_ERR_INVALID_ARG = -1
@@ -54,6 +55,8 @@ SIGNATURES = {
                                   _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _PDims, _vp, _vp, _i64, _f32, _vp, _i32, _vp,
                                     _vp]),
+    "dbsp_sparse_select_noalloc": (_i32, [_vp, _vp, _PDims, Range, Range, _i32, _f64, _i32, _f32,
+                                          _vp, _vp, _i64, _vp, _vp]),
     "dbsp_sparse_select_strided": (_i32, [_vp, _PStr, _vp, _PStr, _PDims, Range, Range, _i32,
                                           _f64, _i32, _f32, _vp, _vp, _i64, _vp, _vp, _u64,
                                           _vp]),

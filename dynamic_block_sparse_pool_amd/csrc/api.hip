@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/dbsp.h"
 #include "common.hpp"
 
@@ -260,6 +262,38 @@ dbsp::Strides to_strides(const dbsp_strides* s) {
   return dbsp::Strides{s->batch, s->head, s->token};
 }
 
+// Device scratch of dbsp_sparse_select_noalloc, for callers that cannot allocate: one copy of
+// this array per GPU, created when the library's code object is loaded on that GPU and held
+// until the process ends. In host code the name is only a stand-in for the symbol: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, called once per device with that
+// device current, and only that address is ever handed to kernels.
+__device__ __align__(256) unsigned char scratch[DBSP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+int32_t noalloc_scratch(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+    return DBSP_ERR_HIP;
+  if (stream) {  // the stream must run on the current device, whose copy is looked up
+    int sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return DBSP_ERR_HIP;
+    if (sdev != dev) return DBSP_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DBSP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DBSP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,6 +431,25 @@ int32_t dbsp_sparse_select(const void* q, const void* k, const dbsp_dims* dims,
                             dense_extra_blocks, mode, density_or_mass, topk_override, score_scale,
                             row_ptr, col_idx, col_capacity, scores_out, workspace,
                             workspace_bytes, stream);
+}
+
+int32_t dbsp_sparse_select_noalloc(const void* q, const void* k, const dbsp_dims* dims,
+                                   dbsp_range text_blocks, dbsp_range dense_extra_blocks,
+                                   int32_t mode, double density_or_mass, int32_t topk_override,
+                                   float score_scale, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, float* scores_out, void* stream) {
+  // the size check comes first, so a shape too large for the static scratch is refused before
+  // anything touches the GPU
+  if (!shape_ok(dims) || (mode != DBSP_TOPK && mode != DBSP_MASS)) return DBSP_ERR_INVALID_ARG;
+  if (layout_of(dims, mode).total > (uint64_t)DBSP_NOALLOC_SCRATCH_BYTES)
+    return DBSP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int32_t st = noalloc_scratch(stream, &ws);
+  if (st != DBSP_OK) return st;
+  return sparse_select_impl(q, k, dims, nullptr, nullptr, nullptr, text_blocks,
+                            dense_extra_blocks, mode, density_or_mass, topk_override, score_scale,
+                            row_ptr, col_idx, col_capacity, scores_out, ws,
+                            (uint64_t)DBSP_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int32_t dbsp_sparse_select_strided(const void* q, const dbsp_strides* q_strides, const void* k,

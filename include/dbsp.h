@@ -47,7 +47,8 @@
  *   Memory     The caller allocates every buffer (inputs, outputs, CSR, workspace) in device
  *              memory. The library allocates nothing, frees nothing, keeps no state between
  *              calls and never writes its inputs. Calls on different streams with disjoint
- *              output and workspace buffers may overlap.
+ *              output and workspace buffers may overlap. (The one exception is
+ *              dbsp_sparse_select_noalloc, whose scratch is a static device array per GPU.)
  *   Streams    `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work and return
  *              without waiting for it. nnz is left on the device in row_ptr[rows].
  *   Errors     Every argument check runs on the host before anything is launched; a negative
@@ -184,6 +185,30 @@ int32_t dbsp_sparse_select_list(const void* q, const void* k, const dbsp_dims* d
                                 int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                 float* scores_out, void* workspace, uint64_t workspace_bytes,
                                 void* stream);
+
+/*
+ * dbsp_sparse_select without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). It allocates nothing and frees nothing: its scratch (the pooled keys; in
+ * DBSP_MASS mode also per-row counts and bitmasks) lives in a static device array of
+ * DBSP_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held from the library's first use on that
+ * GPU until the process ends; its address is looked up once per device on the first call.
+ * Every argument and result is as dbsp_sparse_select; the caller still passes the CSR and
+ * scores_out buffers. No scratch content needs to be zero on entry; each call leaves its own.
+ * Calls that overlap in time on one GPU (different streams or host threads) share that
+ * scratch and race: serialise them, or use dbsp_sparse_select with a workspace per stream.
+ * The stream must belong to the current device (NULL = the null stream of the current device).
+ * Errors: as dbsp_sparse_select, plus DBSP_ERR_WORKSPACE when the shape needs more scratch than
+ * DBSP_NOALLOC_SCRATCH_BYTES (dbsp_select_workspace_bytes gives the need; it is checked before
+ * any GPU work), DBSP_ERR_INVALID_ARG for a stream of another device, DBSP_ERR_HIP when the
+ * scratch address cannot be looked up.
+ */
+#define DBSP_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB per GPU                             */
+int32_t dbsp_sparse_select_noalloc(const void* q, const void* k, const dbsp_dims* dims,
+                                   dbsp_range text_blocks, dbsp_range dense_extra_blocks,
+                                   int32_t mode, double density_or_mass, int32_t topk_override,
+                                   float score_scale, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, float* scores_out, void* stream);
 
 /*
  * dbsp_sparse_select on strided Q and K views (dbsp_strides, in elements of the input dtype):

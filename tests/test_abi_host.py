@@ -372,3 +372,21 @@ def test_row_order_calls_reject_bad_arguments(lib):
 
     assert attn(row_order=None) == E.DBSP_ERR_INVALID_ARG
     assert attn(rp=None) == E.DBSP_ERR_INVALID_ARG
+
+
+def test_noalloc_select_rejects_before_gpu_work(lib):
+    # the size check of the static scratch and the argument checks run on the host first
+    w = WORKLOADS["final_720p_clip2"]
+    big = dims_of(w, heads=64)              # ~37 MiB of pooled keys > the 32 MiB scratch
+    need = ctypes.c_uint64()
+    assert lib.dbsp_select_workspace_bytes(ctypes.byref(big), _abi.DBSP_TOPK,
+                                           ctypes.byref(need)) == 0
+    assert need.value > _abi.DBSP_NOALLOC_SCRATCH_BYTES
+    args = (_abi.Range(0, 4), _abi.Range(0, 0), _abi.DBSP_TOPK, 0.09375, -1, 0.0, FAKE, FAKE,
+            1 << 30, None, None)
+    assert lib.dbsp_sparse_select_noalloc(FAKE, FAKE, ctypes.byref(big), *args) == \
+        _abi.DBSP_ERR_WORKSPACE
+    assert lib.dbsp_sparse_select_noalloc(FAKE, FAKE, None, *args) == _abi.DBSP_ERR_INVALID_ARG
+    bad_mode = (args[0], args[1], 7) + args[3:]
+    assert lib.dbsp_sparse_select_noalloc(FAKE, FAKE, ctypes.byref(dims_of(w)), *bad_mode) == \
+        _abi.DBSP_ERR_INVALID_ARG
