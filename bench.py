@@ -90,6 +90,8 @@ def parse():
                          "held-out input; anchor: the anchor-row path of repeating heads on "
                          "the DiT geometry (one JSON line each)")
     ap.add_argument("--inputs", type=int, default=16, help="calibrate: calibration inputs")
+    ap.add_argument("--bound-rows", type=int, default=8,
+                    help="energy: sampled rows for the token-wise upper bound (0 skips it)")
     ap.add_argument("--row-order", choices=("auto", "row", "lpt"), default="auto",
                     help="attention row order: longest first (lpt, built after each selection "
                          "and timed with it) or row order; auto = lpt in mass mode")
@@ -299,9 +301,43 @@ def energy_suite(args, torch):
                         "mean_retained_mass": round(float(mass_pooled.mean()), 5),
                         "min_retained_mass": round(float(mass_pooled.min()), 5)},
     }
+    if args.bound_rows > 0:
+        res["token_upper_bound"] = token_bound_sample(w, q, k, pooled, mass_pooled,
+                                                      args.bound_rows, args.seed)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = energy_cpu_baseline(w, q, k, flop, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def token_bound_sample(w, q, k, index, mass_gpu, n_rows, seed):
+    """The comparison behind SparSTAR's Figure 3: on sampled rows of one head, the attention mass
+    the hot path's block mask keeps (from the GPU's token-level energies) against the token-wise
+    upper bound for the same token budget (the oracle: each query keeps its own largest
+    probabilities, as many keys as the block mask gives it). The gap is bound - block mass."""
+    import numpy as np
+    import oracle
+    h = w.heads // 2
+    nqb = w.n_q_blocks
+    rng = np.random.default_rng(seed + 11)
+    qi = sorted(rng.choice(nqb, size=min(n_rows, nqb), replace=False).tolist())
+    rp = index.row_ptr.cpu().numpy().astype(np.int64)
+    rows = [h * nqb + i for i in qi]                        # batch 0, head h
+    kept = [int(rp[r + 1] - rp[r]) for r in rows]
+    budgets = [128 * n for n in kept]
+    qh = q[0:1, h:h + 1].double().cpu().numpy()
+    kh = k[0:1, h:h + 1].double().cpu().numpy()
+    t0 = time.perf_counter()
+    bound = oracle.token_upper_bound(qh, kh, qi, budgets)
+    t = time.perf_counter() - t0
+    block = mass_gpu.cpu().numpy()[rows]
+    gap = bound - block
+    return {"head": h, "rows": qi, "kept_blocks": kept,
+            "block_mass": [round(float(x), 5) for x in block],
+            "bound": [round(float(x), 5) for x in bound],
+            "mean_block_mass": round(float(block.mean()), 5),
+            "mean_bound": round(float(bound.mean()), 5),
+            "mean_gap": round(float(gap.mean()), 5), "max_gap": round(float(gap.max()), 5),
+            "oracle_s": round(t, 1)}
 
 
 def calibrate_suite(args, torch):
