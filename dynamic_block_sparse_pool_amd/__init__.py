@@ -23,7 +23,7 @@ from . import _abi
 from ._abi import DBSP_BLOCK, DbspError
 
 __all__ = ["BlockIndex", "sparse_select", "sparse_attn_fwd", "lpt_order", "topk_budget",
-           "select_nnz_bound", "select_workspace_bytes", "block_energy", "retained_mass", "select_energy",
+           "select_nnz_bound", "select_workspace_bytes", "block_energy", "block_energy_workspace_bytes", "retained_mass", "select_energy",
            "MaskVote", "anchor_attn_fwd", "to_intervals", "from_intervals",
            "DbspError", "DBSP_BLOCK", "version"]
 
@@ -344,11 +344,24 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Bl
     return (out, lse) if return_lse else out
 
 
+def block_energy_workspace_bytes(q: torch.Tensor, k: torch.Tensor) -> int:
+    """Workspace size (bytes) at which block_energy runs with all its workgroups at once (0 for
+    float32 inputs)."""
+    dims = _dims(q, k)
+    need = ctypes.c_uint64()
+    _abi.check(_abi.load().dbsp_block_energy_workspace_bytes(ctypes.byref(dims),
+                                                             ctypes.byref(need)),
+               "dbsp_block_energy_workspace_bytes")
+    return need.value
+
+
 def block_energy(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0,
-                 return_lse: bool = False, out: Optional[torch.Tensor] = None):
+                 return_lse: bool = False, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
     """Token-level block energy of every (query block, key block) pair of each head: the
     attention probability mass between the two blocks under the dense softmax over all keys,
-    divided by 128. Returns a float32 [rows, n_k_blocks] tensor (and the per-query lse)."""
+    divided by 128. Returns a float32 [rows, n_k_blocks] tensor (and the per-query lse).
+    `workspace` (uint8, on q's device) is allocated at block_energy_workspace_bytes when None."""
     _check_device_tensor("q", q)
     _check_device_tensor("k", k)
     dims = _dims(q, k)
@@ -359,9 +372,16 @@ def block_energy(q: torch.Tensor, k: torch.Tensor, softmax_scale: float = 0.0,
     elif out.shape != (rows, nkb) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 [rows, n_k_blocks] tensor")
     _check_on("out", out, q.device)
+    if workspace is None:
+        need = block_energy_workspace_bytes(q, k)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _check_on("workspace", workspace, q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     st = _abi.load().dbsp_block_energy(_ptr(q), _ptr(k), ctypes.byref(dims), float(softmax_scale),
-                                       _ptr(out), _ptr(lse), _stream(q.device))
+                                       _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                       _stream(q.device))
     _abi.check(st, "dbsp_block_energy")
     return (out, lse) if return_lse else out
 

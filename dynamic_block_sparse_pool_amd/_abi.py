@@ -70,7 +70,8 @@ SIGNATURES = {
                                        _vp, _vp, _i64, _vp, _vp, _u64, _vp]),
     "dbsp_select_nnz_bound_list": (_i32, [_PDims, _i32, _f64, _vp, _i32, _i32,
                                           ctypes.POINTER(_i64)]),
-    "dbsp_block_energy": (_i32, [_vp, _vp, _PDims, _f32, _vp, _vp, _vp]),
+    "dbsp_block_energy_workspace_bytes": (_i32, [_PDims, ctypes.POINTER(_u64)]),
+    "dbsp_block_energy": (_i32, [_vp, _vp, _PDims, _f32, _vp, _vp, _vp, _u64, _vp]),
     "dbsp_retained_mass": (_i32, [_vp, _PDims, _vp, _vp, _i64, _vp, _vp]),
     "dbsp_select_energy": (_i32, [_vp, _PDims, Range, Range, _f64, _vp, _vp, _i64, _vp, _u64,
                                   _vp]),

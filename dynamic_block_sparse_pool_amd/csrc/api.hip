@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/dbsp.h"
@@ -227,6 +228,12 @@ int32_t anchor_layout(const dbsp_dims* d, int32_t frames, int32_t rows, int32_t 
   l.total = off;
   *out = l;
   return DBSP_OK;
+}
+
+// Workspace of one persistent workgroup of the bf16 energy kernel: a float per (key block,
+// query of a block).
+uint64_t energy_slot_bytes(const dbsp_dims* dims) {
+  return (uint64_t)nkb_of(dims) * dbsp::kBlock * sizeof(float);
 }
 
 // dbsp_select_energy: per-row counts and kept bitmasks only.
@@ -603,8 +610,19 @@ int32_t dbsp_sparse_attn_fwd_strided(const void* q, const dbsp_strides* q_stride
                    col_capacity, softmax_scale, o, o_strides, o_dtype, lse_out, nullptr, stream);
 }
 
+int32_t dbsp_block_energy_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes) {
+  if (!shape_ok(dims) || !bytes) return DBSP_ERR_INVALID_ARG;
+  if (!attn_supported(dims) || nkb_of(dims) > DBSP_MAX_KEY_BLOCKS) return DBSP_ERR_UNSUPPORTED;
+  const int64_t rows = rows_of(dims);
+  *bytes = dims->dtype == DBSP_BF16
+               ? (uint64_t)std::min<int64_t>(rows, dbsp::kEnergySlots) * energy_slot_bytes(dims)
+               : 0;
+  return DBSP_OK;
+}
+
 int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, float softmax_scale,
-                          float* energy, float* lse_out, void* stream) {
+                          float* energy, float* lse_out, void* workspace,
+                          uint64_t workspace_bytes, void* stream) {
   if (!shape_ok(dims) || !q || !k || !energy) return DBSP_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || ((uintptr_t)energy & 3u) || ((uintptr_t)lse_out & 3u))
     return DBSP_ERR_INVALID_ARG;
@@ -624,6 +642,13 @@ int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, f
   a.scale_log2 = scale * 1.4426950408889634f;
   a.energy = energy;
   a.lse = lse_out;
+  if (dims->dtype == DBSP_BF16) {  // one slot per persistent workgroup, as many as fit
+    const uint64_t per_slot = energy_slot_bytes(dims);
+    a.slots = std::min<int64_t>(std::min<int64_t>(a.rows, dbsp::kEnergySlots),
+                                (int64_t)std::min<uint64_t>(workspace_bytes / per_slot, INT64_MAX));
+    if (!workspace || a.slots < 1 || ((uintptr_t)workspace & 255u)) return DBSP_ERR_WORKSPACE;
+    a.ws = static_cast<float*>(workspace);
+  }
   if (dbsp::launch_energy(a, dims->head_dim, dims->dtype == DBSP_BF16,
                           static_cast<hipStream_t>(stream)) != hipSuccess)
     return DBSP_ERR_HIP;

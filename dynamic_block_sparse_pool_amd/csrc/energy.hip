@@ -9,52 +9,52 @@
 // blocks).
 //
 // block_energy_bf16_kernel (bf16, head_dim 128): one workgroup of 4 waves per (batch, head,
-// query block) row, wave w owning queries [32 w, 32 w + 32) with the same S^T = K Q^T tiling on
-// 32x32x16 bf16 MFMAs as the attention kernel. Two sweeps over every key block of the head:
-//   1. a running sum of exp2(s - m) per query against a lazily raised reference m, giving its
-//      log-sum-exp (log2 units);
-//   2. per key block, the sum of exp2(s - lse) over the block's 128 x 128 pairs: each lane adds
-//      its 64 values, the wave adds its lanes in a fixed DPP order, and the four wave totals are
-//      added in wave order and divided by 128 (deterministic, no atomics).
-// K tiles are double-buffered in LDS: the DMA of the next block runs while this one is scored.
-// Every row of a head walks the same blocks in the same order, so the K stream is shared
-// through L2 by the workgroups of a head that run together.
+// query block) row at a time, wave w owning queries [32 w, 32 w + 32) with the same S^T = K Q^T
+// tiling on 32x32x16 bf16 MFMAs as the attention kernel, and one sweep over every key block of
+// the head: per query it keeps a running sum of exp2(s - m) against a lazily raised reference m
+// (its log-sum-exp at the end) and, per key block, log2 of the block's sum of exp2(s), which it
+// parks in a workspace slot of its own; after the sweep the block energies are formed from those
+// and the log-sum-exps (each lane adds two queries, the wave adds its lanes in a fixed DPP
+// order: deterministic, no atomics). K tiles are double-buffered in LDS: the DMA of the next
+// block runs while this one is scored. Every row of a head walks the same blocks in the same
+// order, so the K stream is shared through L2 by the workgroups of a head that run together.
 //
 // block_energy_f32_kernel (fp32, head_dim 64 or 128): one thread per query, K block in LDS,
-// the same two sweeps with plain FMA arithmetic and a tree reduction per key block.
+// two sweeps (log-sum-exp, then the block sums against it) with plain FMA arithmetic and a tree
+// reduction per key block.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
 
 namespace dbsp {
 
-// Step g of the 2 * n steps over the n whole key blocks (block g mod n) lives in LDS buffer
-// g & 1. Waits for it, lets every wave finish the previous step, and starts the DMA of step g + 1
-// into the other buffer (the final step re-fetches its own block: an unconditional issue keeps
-// the compiler's DMA wait tracking exact).
-__device__ __forceinline__ const uint16_t* energy_step_begin(int g, int n, uint16_t* k_lds,
-                                                             __amdgpu_buffer_rsrc_t kbuf, int w,
-                                                             const DmaOffsets& dmo) {
+// Step g over the n whole key blocks (block g) reads `cur`, whose DMA was issued one step
+// earlier: waits for it, lets every wave finish the previous step (which read `next`), and
+// starts the DMA of block g + 1 into `next` (the final step re-fetches its own block: an
+// unconditional issue keeps the DMA wait tracking simple). `cur` and `next` are two separate
+// LDS arrays chosen at compile time, so the compiler can tell the DMA into one from the reads of
+// the other and leaves the prefetch in flight across the step's LDS reads.
+__device__ __forceinline__ void energy_step_begin(int g, int n, uint16_t* next,
+                                                  __amdgpu_buffer_rsrc_t kbuf, int w,
+                                                  const DmaOffsets& dmo) {
   constexpr int kTileBytes = kBlock * 128 * 2;
   wait_vmcnt<0>();
   wait_lgkmcnt0();
   wg_barrier();
-  const int gn = g + 1 < 2 * n ? g + 1 : g;
-  const int cn = gn < n ? gn : gn - n;
-  tile_dma<false>(kbuf, cn * kTileBytes, k_lds + ((g + 1) & 1) * (kBlock * 128), w, dmo, 256);
-  return k_lds + (g & 1) * (kBlock * 128);
+  const int cn = g + 1 < n ? g + 1 : g;
+  tile_dma<false>(kbuf, cn * kTileBytes, next, w, dmo, 256);
 }
 
-// The partial last key block (keys [0, klast) of it exist) goes through plain loads into LDS
-// buffer `buf`, outside the DMA pipeline; keys past klast are masked to -inf.
-__device__ __forceinline__ const uint16_t* energy_tail_tile(const uint16_t* ktail, int klast,
-                                                            uint16_t* k_lds, int buf, int tid) {
+// The partial last key block (keys [0, klast) of it exist) goes through plain loads into LDS,
+// outside the DMA pipeline, once every wave is done with the tile and the DMAs have landed;
+// keys past klast are masked to -inf.
+__device__ __forceinline__ void energy_tail_tile(const uint16_t* ktail, int klast,
+                                                 uint16_t* tile, int tid) {
+  wait_vmcnt<0>();
   wait_lgkmcnt0();
-  wg_barrier();  // every wave is done with buffer `buf`
-  uint16_t* kt = k_lds + buf * (kBlock * 128);
-  tile_load_partial<false>(ktail, klast, kt, tid, 128);
+  wg_barrier();
+  tile_load_partial<false>(ktail, klast, tile, tid, 128);
   __syncthreads();
-  return kt;
 }
 
 __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[4], int h, int klast) {
@@ -65,7 +65,7 @@ __device__ __forceinline__ void mask_tail(f32x16 (&sacc)[4], int h, int klast) {
       if (sacc_key(jt, r, h) >= klast) sacc[jt][r] = -INFINITY;
 }
 
-// Sweep 1 on one S^T tile: running sum per query of exp2(s - m_run) against a lazily raised
+// One S^T tile of the sweep: running sum per query of exp2(s - m_run) against a lazily raised
 // reference m_run (log2 units). The tile's terms are added against the current reference
 // first; the reference is kept while every lane's partial sum over the tile (64 terms) stays at
 // or below kLseSumLimit, which bounds every term by it. Only when a tile breaks the bound, or the
@@ -88,8 +88,8 @@ __device__ __forceinline__ float lse_terms(const f32x16 (&sacc)[4], float scale_
   return ps;
 }
 
-__device__ __forceinline__ void lse_update(const f32x16 (&sacc)[4], float scale_log2, float& m_run,
-                                           float& l_run) {
+__device__ __forceinline__ float lse_update(const f32x16 (&sacc)[4], float scale_log2,
+                                            float& m_run, float& l_run) {
   float ps = lse_terms(sacc, scale_log2, m_run);
   // !(x <= limit) is also true for NaN and +inf sums
   if (__ballot(m_run == -INFINITY || !(ps <= kLseSumLimit)) != 0ull) {
@@ -106,111 +106,173 @@ __device__ __forceinline__ void lse_update(const f32x16 (&sacc)[4], float scale_
     ps = lse_terms(sacc, scale_log2, m_run);
   }
   l_run += ps;
+  return ps;  // the lane's terms of this tile against the (possibly raised) m_run
 }
 
-// Sweep 2 on the S^T tile of key block c: the wave's probability total for c lands in lane
-// c mod 64 of `acc`; every 64 blocks (and after the last one) the four wave totals are added in
-// wave order, divided by the number of queries of the block, and written.
-__device__ __forceinline__ void energy_update(const f32x16 (&sacc)[4], float scale_log2,
-                                              float lse2, bool q_valid, int c, int nkb, int lane,
-                                              int w, float (*part)[64], float& acc, float* erow,
-                                              float qcount) {
-  float ps = 0.f;
+// The query's log2-sum over one key block: lse_update on the block's S^T tile, then
+// m_run + log2 of the block's terms (lanes l32 and l32 + 32 hold the two key halves of the same
+// query and share m_run), i.e. log2 of the sum of exp2(s * scale_log2) over the block's keys,
+// which does not depend on the reference. -inf when the query has no term in the block.
+__device__ __forceinline__ float block_log2sum(const f32x16 (&sacc)[4], float scale_log2,
+                                               float& m_run, float& l_run) {
+  const float ps = lse_update(sacc, scale_log2, m_run, l_run);
+  return m_run + __log2f(ps + __shfl_xor(ps, 32, 64));
+}
+
+// Fragments of sub-tile jt (keys 32 jt .. 32 jt + 31) of a K tile as the A operands of the
+// S^T MFMAs (the layout qk_block reads).
+__device__ __forceinline__ void read_k_subtile(const uint16_t* k_tile, int jt, int l32, int h,
+                                               bf16x8 (&dst)[8]) {
+  const int kr = 32 * jt + l32;
+  const uint16_t* krow = k_tile + kr * 128;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int s = 0; s < 8; ++s)
+    dst[s] = *reinterpret_cast<const bf16x8*>(krow + k_swz(kr, 2 * s + h) * 8);
+}
+
+// qk_block with the LDS reads of sub-tile jt + 1 issued before the MFMAs of sub-tile jt (the
+// scheduling fences keep that order), so the reads of one sub-tile run under the matrix work of
+// the previous one.
+__device__ __forceinline__ void qk_block_pipelined(const uint16_t* k_tile,
+                                                   const bf16x8 (&qf)[8], int l32, int h,
+                                                   f32x16 (&sacc)[4]) {
+  bf16x8 ka[2][8];
+  read_k_subtile(k_tile, 0, l32, h, ka[0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], scale_log2, -lse2));
-  const float t = wave_total_f32(q_valid ? ps : 0.f);
-  acc = lane == (c & 63) ? t : acc;
-  if ((c & 63) == 63 || c == nkb - 1) {  // uniform: flush 64 blocks (or the tail)
-    part[w][lane] = acc;
-    wait_lgkmcnt0();
-    wg_barrier();
-    const int cc = (c & ~63) + lane;
-    if (w == 0 && cc <= c)
-      erow[cc] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / qcount;
+  for (int jt = 0; jt < 4; ++jt) {
+    if (jt + 1 < 4) read_k_subtile(k_tile, jt + 1, l32, h, ka[(jt + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[jt & 1][s], qf[s], sacc[jt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// One sweep per row. For each (batch, head, query block) row the workgroup walks every key
+// block once; per query t and key block c it keeps b[c][t] = log2 sum over the block's keys of
+// exp2(s * scale_log2) (block_log2sum) in its own slot of the workspace, and the running
+// log-sum-exp of the query. Once the sweep ends, energy[row][c] = (1 / n) * sum over the block's
+// queries of exp2(b[c][t] - lse_t): Eq. (5) with each query's probabilities summed per key
+// block first. The dense Q K^T product is formed once (the two-pass alternative forms it twice:
+// once for the log-sum-exp, once for the block sums against it).
+//
+// Persistent: gridDim.x workgroups (at most rows), workgroup g taking rows g, g + gridDim.x, ...,
+// each owning the nkb * 128 floats at ws + g * nkb * 128, written during a row's sweep and read
+// back by the same workgroup after it; rows run in the same order across the grid as a
+// one-row-per-workgroup launch would dispatch them, so the workgroups of one XCD still sweep the
+// same head's K together (through L2). The b values of block c are stored at the start of step
+// c + 1, next to the DMA of block c + 2, so the step's vector-memory wait covers both.
+// Per block, each lane adds 64 terms, the two halves of a query meet by a lane swap, and the
+// energies add 128 queries in a fixed DPP order: results are bit-reproducible.
 __global__ __launch_bounds__(256, 2) void block_energy_bf16_kernel(
     const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg, int nqb, int nkb,
-    int64_t lq, int64_t lk, float scale_log2, float* __restrict__ energy,
-    float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * kBlock * 128];
-  __shared__ float part[4][64];
+    int64_t lq, int64_t lk, int64_t rows, float scale_log2, float* __restrict__ energy,
+    float* __restrict__ lse, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(1024))) uint16_t k0[kBlock * 128];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1[kBlock * 128];
+  __shared__ float lse_s[kBlock];
 
-  const int64_t row = blockIdx.x;
-  const int64_t bh = row / nqb;
-  const int qb = (int)(row - bh * nqb);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kg + bh * lk * 128, (uint32_t)(lk * 256));
+  const int qoff = 32 * w + l32;
   const DmaOffsets dmo = dma_offsets(lane, 256, 256);
   // whole key blocks go through the DMA pipeline; a partial last one is handled apart
   const int klast = (int)(lk - (int64_t)(nkb - 1) * kBlock);
   const bool has_tail = klast < kBlock;
   const int nfull = has_tail ? nkb - 1 : nkb;
-  const uint16_t* ktail = kg + (bh * lk + (int64_t)(nkb - 1) * kBlock) * 128;
-  const int qcount_i = (int)(lq - (int64_t)qb * kBlock < kBlock ? lq - (int64_t)qb * kBlock
-                                                                : kBlock);
-  const float qcount = (float)qcount_i;
+  float* __restrict__ slot = ws + (int64_t)blockIdx.x * nkb * kBlock;
 
-  // Q^T as the B operand: lane (h, l32) holds query 32 w + l32, dims 16 s + 8 h .. +7; queries
-  // past lq are zero and add nothing to the energies
-  const int64_t qi = (int64_t)qb * kBlock + 32 * w + l32;
-  const bool q_valid = qi < lq;
-  const int64_t qtok = bh * lq + qi;
-  bf16x8 qf[8];
-  {
-    const uint16_t* qr = qg + (q_valid ? qtok : bh * lq) * 128 + 8 * h;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int64_t bh = row / nqb;
+    const int qb = (int)(row - bh * nqb);
+    const __amdgpu_buffer_rsrc_t kbuf = raw_buffer(kg + bh * lk * 128, (uint32_t)(lk * 256));
+    const uint16_t* ktail = kg + (bh * lk + (int64_t)(nkb - 1) * kBlock) * 128;
+    const int qcount_i = (int)(lq - (int64_t)qb * kBlock < kBlock ? lq - (int64_t)qb * kBlock
+                                                                  : kBlock);
+
+    // Q^T as the B operand: lane (h, l32) holds query 32 w + l32, dims 16 s + 8 h .. +7; queries
+    // past lq are zero and their block sums are stored as -inf (no contribution)
+    const int64_t qi = (int64_t)qb * kBlock + qoff;
+    const bool q_valid = qi < lq;
+    const int64_t qtok = bh * lq + qi;
+    bf16x8 qf[8];
+    {
+      const uint16_t* qr = qg + (q_valid ? qtok : bh * lq) * 128 + 8 * h;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
-      qf[s] = q_valid ? v : bf16x8{};
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
+        qf[s] = q_valid ? v : bf16x8{};
+      }
     }
-  }
 
-  if (nfull > 0) tile_dma<false>(kbuf, 0, k_lds, w, dmo, 256);
+    if (nfull > 0) tile_dma<false>(kbuf, 0, k0, w, dmo, 256);
 
-  // sweep 1: log-sum-exp per query (lanes l32 and l32 + 32 hold halves of the same query)
-  float m_run = -INFINITY, l_run = 0.f;
-  for (int g = 0; g < nfull; ++g) {
-    const uint16_t* kt = energy_step_begin(g, nfull, k_lds, kbuf, w, dmo);
-    f32x16 sacc[4];
-    qk_block(kt, qf, l32, h, sacc);
-    lse_update(sacc, scale_log2, m_run, l_run);
-  }
-  if (has_tail) {  // the DMA in flight (block 0 of sweep 2) targets buffer nfull & 1
-    const uint16_t* kt = energy_tail_tile(ktail, klast, k_lds, (nfull & 1) ^ 1, tid);
-    f32x16 sacc[4];
-    qk_block(kt, qf, l32, h, sacc);
-    mask_tail(sacc, h, klast);
-    lse_update(sacc, scale_log2, m_run, l_run);
-  }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float lse2 = m_run + __log2f(l_tot);
-  if (lse && h == 0 && q_valid) lse[qtok] = lse2 * 0.69314718055994531f;
+    // step g: block g from k0 (g even) or k1 (g odd); its b goes out at step g + 1
+    float m_run = -INFINITY, l_run = 0.f, b_prev = -INFINITY;
+#define DBSP_ENERGY_STEP(G, CUR, NEXT)                                                        \
+  do {                                                                                        \
+    energy_step_begin((G), nfull, (NEXT), kbuf, w, dmo);                                      \
+    if ((G) > 0 && h == 0) slot[(int64_t)((G) - 1) * kBlock + qoff] = b_prev;                 \
+    f32x16 sacc[4];                                                                           \
+    qk_block_pipelined((CUR), qf, l32, h, sacc);                                              \
+    const float b = block_log2sum(sacc, scale_log2, m_run, l_run);                            \
+    b_prev = q_valid ? b : -INFINITY;                                                         \
+  } while (0)
+    int g = 0;
+    for (; g + 1 < nfull; g += 2) {
+      DBSP_ENERGY_STEP(g, k0, k1);
+      DBSP_ENERGY_STEP(g + 1, k1, k0);
+    }
+    if (g < nfull) DBSP_ENERGY_STEP(g, k0, k1);
+#undef DBSP_ENERGY_STEP
+    if (nfull > 0 && h == 0) slot[(int64_t)(nfull - 1) * kBlock + qoff] = b_prev;
+    if (has_tail) {
+      energy_tail_tile(ktail, klast, k0, tid);
+      f32x16 sacc[4];
+      qk_block(k0, qf, l32, h, sacc);
+      mask_tail(sacc, h, klast);
+      const float b = block_log2sum(sacc, scale_log2, m_run, l_run);
+      if (h == 0) slot[(int64_t)(nkb - 1) * kBlock + qoff] = q_valid ? b : -INFINITY;
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float lse2 = m_run + __log2f(l_tot);
+    if (lse && h == 0 && q_valid) lse[qtok] = lse2 * 0.69314718055994531f;
+    if (h == 0) lse_s[qoff] = lse2;
+    wait_vmcnt<0>();  // the slot's stores (and the last re-fetch) complete
+    wait_lgkmcnt0();
+    wg_barrier();
 
-  // sweep 2: block energies
-  float* erow = energy + row * nkb;
-  float acc = 0.f;
-  for (int g = nfull; g < 2 * nfull; ++g) {
-    const uint16_t* kt = energy_step_begin(g, nfull, k_lds, kbuf, w, dmo);
-    f32x16 sacc[4];
-    qk_block(kt, qf, l32, h, sacc);
-    energy_update(sacc, scale_log2, lse2, q_valid, g - nfull, nkb, lane, w, part, acc, erow,
-                  qcount);
-  }
-  if (has_tail) {  // the last step re-fetched its own block into buffer 0
-    const uint16_t* kt = energy_tail_tile(ktail, klast, k_lds, 1, tid);
-    f32x16 sacc[4];
-    qk_block(kt, qf, l32, h, sacc);
-    mask_tail(sacc, h, klast);
-    energy_update(sacc, scale_log2, lse2, q_valid, nkb - 1, nkb, lane, w, part, acc, erow,
-                  qcount);
+    // energies: wave w takes key blocks [64 (4 i + w), + 64), eight blocks' loads in flight;
+    // lane j of the wave ends up with block base + j and the wave stores 64 energies at once
+    const float la = lse_s[2 * lane], lb = lse_s[2 * lane + 1];
+    const float inv_q = 1.0f / (float)qcount_i;
+    float* erow = energy + row * nkb;
+    for (int base = 64 * w; base < nkb; base += 256) {
+      float mine = 0.f;
+      for (int j0 = 0; j0 < 64; j0 += 8) {
+        f32x2 bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = base + j0 + j;  // wave-uniform
+          bv[j] = c < nkb ? *reinterpret_cast<const f32x2*>(slot + (int64_t)c * kBlock + 2 * lane)
+                          : f32x2{-INFINITY, -INFINITY};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = __builtin_amdgcn_exp2f(bv[j][0] - la) + __builtin_amdgcn_exp2f(bv[j][1] - lb);
+          const float t = wave_total_f32(e);
+          mine = lane == j0 + j ? t : mine;
+        }
+      }
+      if (base + lane < nkb) erow[base + lane] = mine * inv_q;
+    }
+    wg_barrier();  // lse_s and the slot belong to the next row
   }
   wait_vmcnt<0>();
 }
@@ -308,10 +370,12 @@ __global__ __launch_bounds__(256) void retained_mass_kernel(
 
 hipError_t launch_energy(const EnergyArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   const dim3 grid((unsigned)a.rows);
-  if (bf16 && head_dim == 128)
-    block_energy_bf16_kernel<<<grid, 256, 0, stream>>>(
+  if (bf16 && head_dim == 128) {
+    if (a.slots < 1 || a.slots > a.rows || !a.ws) return hipErrorInvalidValue;
+    block_energy_bf16_kernel<<<dim3((unsigned)a.slots), 256, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), a.nqb, a.nkb, a.lq,
-        a.lk, a.scale_log2, a.energy, a.lse);
+        a.lk, a.rows, a.scale_log2, a.energy, a.lse, a.ws);
+  }
   else if (!bf16 && head_dim == 64)
     block_energy_f32_kernel<64><<<grid, kBlock, 0, stream>>>(a);
   else if (!bf16 && head_dim == 128)

@@ -77,7 +77,13 @@ struct EnergyArgs {
   float scale_log2;  // softmax_scale * log2(e)
   float* energy;     // [rows, nkb]
   float* lse;        // nullable [rows * 128]
+  float* ws;         // bf16 path: slots * nkb * 128 floats (per-query block log2-sums)
+  int64_t slots;     // bf16 path: persistent workgroups, 1 .. rows
 };
+
+// Workgroups of the one-sweep bf16 energy kernel that a full workspace provides for: two per
+// compute unit of a 256-CU device.
+constexpr int64_t kEnergySlots = 512;
 
 // Query geometry of the anchor-row path: frames x rows x width tokens, then trailing tokens.
 struct AnchorGeom {

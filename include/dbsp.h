@@ -313,20 +313,30 @@ int32_t dbsp_row_order_lpt(const int32_t* row_ptr, const dbsp_dims* dims, int64_
  *   n_i = the number of queries block i holds (128 unless it is a partial last block),
  *   P_tj = softmax over ALL lk keys of (q_t . k_j * softmax_scale)
  * so each row sums to 1 (up to rounding). softmax_scale <= 0 means 1 / sqrt(head_dim). The
- * attention matrix is never stored: the kernel makes two passes over the keys (log-sum-exp per
- * query, then the block sums). Arithmetic as dbsp_sparse_attn_fwd (bf16 matrix-core products
- * with float32 accumulation; float32 for float32 inputs); the block sums add in a fixed order,
- * so results are bit-reproducible.
+ * attention matrix is never stored. bf16: one pass over the keys per row, keeping per query its
+ * log-sum-exp and, per key block, the log of that block's sum of exponentials (in the
+ * workspace); the energies follow from the two once the pass ends. float32: two passes
+ * (log-sum-exp per query, then the block sums against it), no workspace. Arithmetic as
+ * dbsp_sparse_attn_fwd (bf16 matrix-core products with float32 accumulation; float32 for
+ * float32 inputs); sums add in a fixed order, so results are bit-reproducible.
  *
  * q, k: as for dbsp_sparse_attn_fwd (no V). energy: device float32 [rows, lk / 128].
  * lse_out, if not NULL: device float32 [batch, heads, lq], the natural-log log-sum-exp of each
- * query over all keys. Cost: 4 * 128 * 128 * head_dim FLOP per (row, key block) pair, i.e. the
- * dense QK^T product twice.
+ * query over all keys.
+ * workspace: device memory, 256-byte aligned, contents ignored and overwritten; bf16 inputs
+ * need at least lk / 128 * 512 bytes (one workgroup's slot; more slots run more workgroups at
+ * once, up to the size dbsp_block_energy_workspace_bytes reports, min(rows, 512) slots); float32
+ * inputs need none (NULL and 0 accepted). Calls that share a workspace must not overlap.
+ * Cost: 2 * 128 * 128 * head_dim FLOP per (row, key block) pair for bf16 (the dense QK^T
+ * product once), twice that for float32.
  * Errors: DBSP_ERR_INVALID_ARG for null or misaligned pointers, a bad shape or a non-finite
- * scale; DBSP_ERR_UNSUPPORTED for other dtype / head_dim pairs or lk / 128 > DBSP_MAX_KEY_BLOCKS.
+ * scale; DBSP_ERR_UNSUPPORTED for other dtype / head_dim pairs or lk / 128 > DBSP_MAX_KEY_BLOCKS;
+ * DBSP_ERR_WORKSPACE for a missing, misaligned or too small workspace (bf16).
  */
+int32_t dbsp_block_energy_workspace_bytes(const dbsp_dims* dims, uint64_t* bytes);
 int32_t dbsp_block_energy(const void* q, const void* k, const dbsp_dims* dims, float softmax_scale,
-                          float* energy, float* lse_out, void* stream);
+                          float* energy, float* lse_out, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
 
 /*
  * Retained attention mass of a block mask ([SparSTAR] Figures 3 and 4 report it per scale and

@@ -177,8 +177,8 @@ def test_energy_calls_reject_bad_arguments(lib):
     E = _abi
     good = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_BF16)
 
-    def energy(dims=good, q=FAKE, k=FAKE, out=FAKE, lse=None, scale=0.0):
-        return lib.dbsp_block_energy(q, k, ctypes.byref(dims), scale, out, lse, None)
+    def energy(dims=good, q=FAKE, k=FAKE, out=FAKE, lse=None, scale=0.0, ws=FAKE, ws_n=1 << 20):
+        return lib.dbsp_block_energy(q, k, ctypes.byref(dims), scale, out, lse, ws, ws_n, None)
 
     for kw in ({"q": None}, {"k": None}, {"out": None}, {"scale": float("nan")},
                {"q": ctypes.c_void_p((1 << 20) + 8)}, {"out": ctypes.c_void_p((1 << 20) + 2)},
@@ -186,6 +186,20 @@ def test_energy_calls_reject_bad_arguments(lib):
         assert energy(**kw) == E.DBSP_ERR_INVALID_ARG, kw
     assert energy(dims=_abi.Dims(1, 2, 256, 1024, 64, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
     assert energy(dims=_abi.Dims(1, 1, 256, 2049 * 128, 128, E.DBSP_BF16)) == E.DBSP_ERR_UNSUPPORTED
+    # bf16 needs at least one workgroup's slot (8 key blocks x 128 queries x 4 bytes), 256-aligned
+    for kw in ({"ws": None}, {"ws_n": 8 * 512 - 1}, {"ws": ctypes.c_void_p((1 << 20) + 16)}):
+        assert energy(**kw) == E.DBSP_ERR_WORKSPACE, kw
+
+    need = ctypes.c_uint64()
+    assert lib.dbsp_block_energy_workspace_bytes(ctypes.byref(good), ctypes.byref(need)) == E.DBSP_OK
+    assert need.value == 4 * 8 * 512  # min(rows = 4, 512) slots of 8 blocks x 128 floats
+    big = _abi.Dims(1, 40, 75648, 75648, 128, E.DBSP_BF16)  # 23,640 rows: 512 slots
+    assert lib.dbsp_block_energy_workspace_bytes(ctypes.byref(big), ctypes.byref(need)) == E.DBSP_OK
+    assert need.value == 512 * 591 * 512
+    f32 = _abi.Dims(1, 2, 256, 1024, 128, E.DBSP_F32)
+    assert lib.dbsp_block_energy_workspace_bytes(ctypes.byref(f32), ctypes.byref(need)) == E.DBSP_OK
+    assert need.value == 0
+    assert lib.dbsp_block_energy_workspace_bytes(None, ctypes.byref(need)) == E.DBSP_ERR_INVALID_ARG
 
     def mass(dims=good, e=FAKE, rp=FAKE, ci=FAKE, cap=16, out=FAKE):
         return lib.dbsp_retained_mass(e, ctypes.byref(dims), rp, ci, cap, out, None)

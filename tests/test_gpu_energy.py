@@ -70,6 +70,37 @@ def test_energy_deterministic():
     assert torch.equal(a, b)
 
 
+def test_energy_workspace_slots():
+    """The bf16 kernel runs one persistent workgroup per workspace slot (a slot holds a float per
+    (key block, query) of the row in progress). Any number of slots gives the same bits: with one
+    slot a single workgroup walks every row, reusing its slot and its LDS row after row; a
+    ragged shape (partial last query and key blocks) checks the stale-slot case, where a row
+    leaves entries the next row must not read."""
+    m = dbsp()
+    for name, lq, lk in (("final_small", None, None), ("star_mid_small", 1000, 2700)):
+        w = small_variants()[name]
+        if lq is not None:
+            w = w.with_(lq=lq, lk=lk)
+        say(f"case slots {name} Lq={w.lq} Lk={w.lk} rows={w.rows}")
+        q, k, _ = make_qkv(w, device="cuda", seed=12)
+        full = m.block_energy_workspace_bytes(q, k)
+        slot = w.n_k_blocks * BLOCK * 4
+        assert full == min(w.rows, 512) * slot
+        e0, l0 = m.block_energy(q, k, return_lse=True)
+        for n in (1, 2, 7, w.rows - 1):
+            ws = torch.empty(n * slot + 100, dtype=torch.uint8, device="cuda")
+            e1, l1 = m.block_energy(q, k, return_lse=True, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(e0, e1), n
+            assert torch.equal(l0, l1), n
+        e_ref = oracle.block_energy_rows(P.host(q), P.host(k), rows=range(w.rows))
+        P.check_token_energy(P.host(e0), e_ref)
+    q, k, _ = make_qkv(small_variants()["final_small"], device="cuda", seed=12)
+    with pytest.raises(m.DbspError):
+        m.block_energy(q, k, workspace=torch.empty(70 * BLOCK * 4 - 1, dtype=torch.uint8,
+                                                   device="cuda"))
+
+
 @pytest.mark.parametrize("name", ["dit_mass_small", "clip1_small", "toy"])
 def test_select_energy_and_retained_mass(name):
     m = dbsp()
