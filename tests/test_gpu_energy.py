@@ -48,7 +48,9 @@ def test_energy_parity(name):
 def test_energy_edge_shapes():
     m = dbsp()
     # one key block: every energy is 1; one query block against many key blocks
-    for lq, lk in ((128, 128), (128, 37 * 128), (5 * 128, 128)):
+    # ... and keys shorter than one block (no whole block: only the partial-tile path runs),
+    # with a partial query block too
+    for lq, lk in ((128, 128), (128, 37 * 128), (5 * 128, 128), (200, 100), (300, 1000)):
         w = small_variants()["star_mid_small"].with_(heads=2, lq=lq, lk=lk)
         say(f"case edge lq={lq} lk={lk}")
         q, k, _ = make_qkv(w, device="cuda", seed=9)
@@ -56,7 +58,7 @@ def test_energy_edge_shapes():
         torch.cuda.synchronize()
         e_ref = oracle.block_energy_rows(P.host(q), P.host(k), rows=range(w.rows))
         P.check_token_energy(e, e_ref)
-        if lk == 128:
+        if w.n_k_blocks == 1:
             np.testing.assert_allclose(e, 1.0, rtol=0, atol=P.TOK_ROW_SUM)
 
 
