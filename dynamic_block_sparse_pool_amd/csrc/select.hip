@@ -288,10 +288,51 @@ __device__ __forceinline__ int radix_digit(const uint32_t (&key)[S], uint32_t pr
   return d;
 }
 
+// The top-byte step of the Top-K threshold search without LDS atomics. Candidate keys of a row
+// tend to share one to three top bytes (sign and high exponent bits), which makes a 256-bin
+// histogram of them collide on a few bins. Walking down from the largest top byte present, count
+// the keys with that byte by ballots until the running count reaches `need`: the same digit,
+// count above and bucket size as radix_digit at shift 24. Gives up (returns false) after
+// kTopWalk bytes, leaving the histogram to decide.
+constexpr int kTopWalk = 4;
+
+template <int S>
+__device__ __forceinline__ bool top_byte_walk(const uint32_t (&key)[S], uint32_t need, int* digit,
+                                              uint32_t* above, uint32_t* bucket) {
+  uint32_t acc = 0;
+  uint32_t bound = 257;  // digits below this are still to visit (+1 encoding: 0 = none)
+#pragma unroll 1
+  for (int it = 0; it < kTopWalk; ++it) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+      const uint32_t d1 = (key[e] >> 24) + 1u;
+      if (key[e] != 0u && d1 < bound) mx = mx > d1 ? mx : d1;
+    }
+    mx = wave_max_u32_dpp(mx);
+    if (mx == 0u) return false;  // no candidate left (cannot happen while need <= candidates)
+    const uint32_t d = mx - 1u;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < S; ++e)
+      cnt += (uint32_t)__popcll(ballot64(key[e] != 0u && (key[e] >> 24) == d));
+    if (acc + cnt >= need) {
+      *digit = (int)d;
+      *above = acc;
+      *bucket = cnt;
+      return true;
+    }
+    acc += cnt;
+    bound = mx;
+  }
+  return false;
+}
+
 // Top-K selection of one row held as S slots per lane; writes col_idx and (lane 0) row_ptr.
 // The K-th largest candidate key T is found one byte at a time, most significant first
-// (radix select); a byte whose bucket holds exactly the remaining count ends the search early.
-// All ballots and shuffles sit in wave-uniform control flow.
+// (radix select; the top byte by top_byte_walk when it settles within kTopWalk steps); a byte
+// whose bucket holds exactly the remaining count ends the search early. All ballots and shuffles
+// sit in wave-uniform control flow.
 template <int S>
 __device__ __forceinline__ void select_topk_row(const SelectArgs& a, const float* srow,
                                                 int64_t row, int lane, uint32_t* hist) {
@@ -321,7 +362,9 @@ __device__ __forceinline__ void select_topk_row(const SelectArgs& a, const float
     exact = false;
     for (int shift = 24; shift >= 0; shift -= 8) {
       uint32_t above, cnt_d;
-      const int d = radix_digit<S>(key, T, shift, need, hist, lane, &above, &cnt_d);
+      int d;
+      if (shift != 24 || !top_byte_walk<S>(key, need, &d, &above, &cnt_d))
+        d = radix_digit<S>(key, T, shift, need, hist, lane, &above, &cnt_d);
       T |= (uint32_t)d << shift;
       need -= above;
       low = shift;

@@ -47,10 +47,11 @@ def oracle_select_on(w: Workload, scores2d: np.ndarray, forced: np.ndarray, topk
     return oracle.select_mass(scores2d, forced, w.param)
 
 
-def full_check_small(w: Workload, seed=3, inputs=None, score_scale=None, out=None):
+def full_check_small(w: Workload, seed=3, inputs=None, score_scale=None, out=None, attention=True):
     """Selection and attention of workload w through the C ABI against the oracle on the same
     values: every score, every mask row and CSR entry, every output and lse. `inputs` may be
-    strided views and `out` a strided fp32 output view (the oracle reads their values)."""
+    strided views and `out` a strided fp32 output view (the oracle reads their values);
+    attention=False stops after the selection checks."""
     say(f"case {w.name} B={w.batch} H={w.heads} Lq={w.lq} Lk={w.lk} d={w.head_dim} {w.dtype} "
         f"{w.mode}={w.param} seed={seed}")
     q, k, v = inputs if inputs is not None else make_qkv(w, device="cuda", seed=seed)
@@ -85,6 +86,8 @@ def full_check_small(w: Workload, seed=3, inputs=None, score_scale=None, out=Non
         ndiff = P.topk_near_tie_ok(kept_gpu, ref["kept"].reshape(-1, nkb),
                                    s_ref.reshape(-1, nkb), forced, tol)
         say(f"  rows differing from the oracle's own masks (near ties only): {ndiff}")
+    if not attention:
+        return idx, o, lse
     o_ref, lse_ref = oracle.attention_rows(qh, kh, vh, rp, ci, scale=1.0 / math.sqrt(w.head_dim))
     o_ref, lse_ref = P.rows_to_tokens(o_ref, lse_ref, w.batch, w.heads, w.lq)
     mx, mean = P.check_attention(P.host(o), P.host(lse), o_ref, lse_ref, w.dtype == "bf16")
@@ -134,6 +137,23 @@ def test_adversarial_ties():
               .to(torch.bfloat16) for _ in range(2))
     vm = make_qkv(wm, device="cuda", seed=1)[2]
     full_check_small(wm, inputs=(qm.contiguous(), km.contiguous(), vm))
+
+
+def test_topk_scores_over_many_magnitudes():
+    # Key blocks scaled by powers of two (2^-12 .. 2^11): the pooled scores of a row spread over
+    # many exponents, so the threshold's top byte is settled by the ballot walk at low density
+    # and by the histogram after the walk gives up at high density. Masks must equal the
+    # oracle's on the GPU's scores either way. Selection only: logits reach ~1e4 here, beyond
+    # the range the attention tolerances are derived for.
+    for density in (0.1875, 0.625):
+        w = small_variants()["star_mid_small"].with_(name=f"magnitudes_{density}", heads=2,
+                                                       param=density)
+        q, k, v = make_qkv(w, device="cuda", seed=21)
+        nb = w.lk // BLOCK
+        scale = torch.tensor([2.0 ** ((j * 7) % 24 - 12) for j in range(nb)], device="cuda")
+        ks = (k.float().reshape(1, w.heads, nb, BLOCK, w.head_dim) * scale[:, None, None])
+        k2 = ks.reshape(k.shape).to(torch.bfloat16).contiguous()
+        full_check_small(w, inputs=(q, k2, v), attention=False)
 
 
 def test_all_equal_scores_keep_lowest_indices():
