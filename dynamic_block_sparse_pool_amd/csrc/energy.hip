@@ -119,34 +119,38 @@ __device__ __forceinline__ float block_log2sum(const f32x16 (&sacc)[4], float sc
   return m_run + __log2f(ps + __shfl_xor(ps, 32, 64));
 }
 
-// Fragments of sub-tile jt (keys 32 jt .. 32 jt + 31) of a K tile as the A operands of the
-// S^T MFMAs (the layout qk_block reads).
-__device__ __forceinline__ void read_k_subtile(const uint16_t* k_tile, int jt, int l32, int h,
-                                               bf16x8 (&dst)[8]) {
-  const int kr = 32 * jt + l32;
-  const uint16_t* krow = k_tile + kr * 128;
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    dst[s] = *reinterpret_cast<const bf16x8*>(krow + k_swz(kr, 2 * s + h) * 8);
-}
-
-// qk_block with the LDS reads of sub-tile jt + 1 issued before the MFMAs of sub-tile jt (the
-// scheduling fences keep that order), so the reads of one sub-tile run under the matrix work of
-// the previous one.
-__device__ __forceinline__ void qk_block_pipelined(const uint16_t* k_tile,
-                                                   const bf16x8 (&qf)[8], int l32, int h,
-                                                   f32x16 (&sacc)[4]) {
-  bf16x8 ka[2][8];
-  read_k_subtile(k_tile, 0, l32, h, ka[0]);
+// The A operands of d slice s (dims 16 s .. 16 s + 15) for the four 32-key sub-tiles of a K tile
+// (the fragments qk_block reads for that slice).
+__device__ __forceinline__ void read_k_slice(const uint16_t* k_tile, int s, int l32, int h,
+                                             bf16x8 (&dst)[4]) {
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
-    if (jt + 1 < 4) read_k_subtile(k_tile, jt + 1, l32, h, ka[(jt + 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
+    const int kr = 32 * jt + l32;
+    dst[jt] = *reinterpret_cast<const bf16x8*>(k_tile + kr * 128 + k_swz(kr, 2 * s + h) * 8);
+  }
+}
+
+// qk_block with the d slices outermost: the four sub-tiles' MFMAs of one slice run back to back
+// on the same Q fragment, as four independent accumulation chains, and the K fragments of slice
+// s + 1 are read under the MFMAs of slice s (the scheduling fences keep that order). Each
+// accumulator still adds its slices in ascending order, so the results equal qk_block's bit for
+// bit.
+__device__ __forceinline__ void qk_block_sd_outer(const uint16_t* k_tile,
+                                                  const bf16x8 (&qf)[8], int l32, int h,
+                                                  f32x16 (&sacc)[4]) {
+  bf16x8 ka[2][4];
+  read_k_slice(k_tile, 0, l32, h, ka[0]);
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[jt][r] = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[jt & 1][s], qf[s], sacc[jt], 0, 0, 0);
+  for (int s = 0; s < 8; ++s) {
+    if (s + 1 < 8) read_k_slice(k_tile, s + 1, l32, h, ka[(s + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+      sacc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][jt], qf[s], sacc[jt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void block_energy_bf16_kernel(
     energy_step_begin((G), nfull, (NEXT), kbuf, w, dmo);                                      \
     if ((G) > 0 && h == 0) slot[(int64_t)((G) - 1) * kBlock + qoff] = b_prev;                 \
     f32x16 sacc[4];                                                                           \
-    qk_block_pipelined((CUR), qf, l32, h, sacc);                                              \
+    qk_block_sd_outer((CUR), qf, l32, h, sacc);                                               \
     const float b = block_log2sum(sacc, scale_log2, m_run, l_run);                            \
     b_prev = q_valid ? b : -INFINITY;                                                         \
   } while (0)
