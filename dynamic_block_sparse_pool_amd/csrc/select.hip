@@ -7,18 +7,18 @@
 // Attention", key design 1 and Eq. (5) (shortest energy-sorted prefix reaching a threshold,
 // restored to block order) and key design 4 (per-query-block skip list).
 //
-// score_select_kernel: one workgroup (8 waves) owns 16 consecutive query blocks of one
-// (batch, head).
-//   Phase 0 mean-pools those 16 query blocks straight from Q (the pooling kernel handles the
+// score_select_kernel: one workgroup (8 waves) owns a tile of 16 (or, in the last generation
+// of workgroups, 8) consecutive query blocks of one (batch, head); see select_tiling.
+//   Phase 0 mean-pools the tile's query blocks straight from Q (the pooling kernel handles the
 //   keys, which every workgroup of the head needs before it can score). Streaming Q here lets
 //   the query traffic overlap the latency-bound scoring and selection of other workgroups.
-//   Phase 1 computes S = qbar kbar^T * scale for the 16 rows against every key block with
+//   Phase 1 computes S = qbar kbar^T * scale for the tile's rows against every key block with
 //   16x16x32 bf16 MFMAs on the hi/lo split of the pooled vectors written by the pooling kernel
 //   (x = hi + lo; S ~ hi.hi + hi.lo + lo.hi accumulated in fp32, relative error near 2^-16 of
 //   |qbar||kbar|). Pooled keys arrive in MFMA operand order, so each operand load is one
 //   contiguous 1 KiB read per wave. Each wave walks key tiles of 16 with the next tile's
 //   operands in flight, and parks the scores in LDS.
-//   Phase 2 gives each wave two rows. A wave holds one row in registers (lane l, slot e -> key
+//   Phase 2 gives each wave up to two rows. A wave holds one row in registers (lane l, slot e -> key
 //   block 64 e + l), maps scores to order-preserving uint32 keys and finds the selection
 //   threshold T most significant bits first: in Top-K mode by radix select on bytes with a
 //   per-wave LDS histogram (stopping when a bucket holds exactly the remaining count), in mass
@@ -80,12 +80,12 @@ __device__ __forceinline__ int search_start(uint32_t kmin, uint32_t kmax, uint32
 }
 
 // Phase 0: wave w mean-pools query blocks row0 + 2 w and row0 + 2 w + 1 of this (batch, head)
-// straight from Q. A token row is kChunks 16-byte chunks; lane l sums chunk l % kChunks of
+// straight from Q, those below row_end (the tile's end). A token row is kChunks 16-byte chunks; lane l sums chunk l % kChunks of
 // every (64 / kChunks)-th token of both blocks, with 16 loads in flight per lane (8 per block),
 // and the means are stored as bf16 hi | lo in qlds [16][2][D], the form the scoring MFMAs read.
 template <typename T, int D>
 __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds, int bh, int row0,
-                                            int lane, int wave) {
+                                            int row_end, int lane, int wave) {
   constexpr int kVec = 16 / (int)sizeof(T);
   constexpr int kChunks = D / kVec;
   constexpr int kRowsPerLoad = 64 / kChunks;
@@ -95,7 +95,7 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
   const int chunk = lane % kChunks;
   const int r0 = lane / kChunks;
   const int rr0 = 2 * wave;
-  const bool live0 = row0 + rr0 < a.nqb, live1 = row0 + rr0 + 1 < a.nqb;
+  const bool live0 = row0 + rr0 < row_end, live1 = row0 + rr0 + 1 < row_end;
   if (!live0) return;
   const int64_t first0 = (int64_t)(row0 + rr0) * kBlock;  // first token of block rr0
   const int64_t st = a.qs.t;                                // elements between tokens
@@ -188,15 +188,15 @@ __device__ __forceinline__ void pool_q_rows(const SelectArgs& a, uint16_t* qlds,
 
 template <int D>
 __device__ __forceinline__ void score_phase(const SelectArgs& a, float* s_lds,
-                                            const uint16_t* qlds, int bh, int row0, int lane,
-                                            int wave) {
+                                            const uint16_t* qlds, int bh, int row0, int row_end,
+                                            int lane, int wave) {
   constexpr int KSTEPS = D / 32;
   const int nkb = a.nkb;
   const int m = lane & 15;   // A row / B column inside the 16x16 tile
   const int kq = lane >> 4;  // which 8-wide k chunk of the 32
   bf16x8 qhi[KSTEPS], qlo[KSTEPS];
   {
-    const bool live = row0 + m < a.nqb;
+    const bool live = row0 + m < row_end;
     const uint16_t* qrow = qlds + m * 2 * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -568,15 +568,73 @@ __device__ __forceinline__ void select_mass_row(const SelectArgs& a, const float
   select_mass_probs<S>(a, val, row, lane, hist);
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin by id, so id b runs on XCD b % 8. Work item
-// w = (head, row tile) is assigned as w = (b % 8) * per_xcd + b / 8: each XCD walks a contiguous
-// range of work items, i.e. whole heads one after another, and keeps the pooled keys of the
-// head it is on (2 * nkb * head_dim * 2 bytes) in its own L2.
-__device__ __forceinline__ bool xcd_work_item(int64_t n_items, int64_t* item) {
-  const int64_t per_xcd = (n_items + 7) / 8;
-  const int64_t b = blockIdx.x;
-  *item = (b % 8) * per_xcd + b / 8;
-  return *item < n_items;
+// Work items of the scoring and selection kernel. Each (batch, head) is cut into nbig tiles of
+// kRowsPerWG query blocks from its start and nsmall tiles of kSmallRows blocks for the rest. The
+// kernel holds 2 workgroups per CU, kSlotsPerXcd on each XCD, and a workgroup's time grows with
+// its tile, so the split follows how full the last generation of long tiles would be: when all
+// of an XCD's long tiles fit in one generation, every tile is short (twice as many workgroups in
+// flight); when the last generation would be at most half full, its rows go into short tiles
+// spread over the slots; otherwise only the rows past a head's last whole long tile are short.
+constexpr int kSmallRows = 8;
+constexpr int64_t kSlotsPerXcd = 64;
+struct SelectTiling {
+  int nbig, nsmall;
+};
+__host__ __device__ inline SelectTiling select_tiling(int64_t n_heads, int nqb) {
+  const int64_t nh = (n_heads + 7) / 8;  // heads of the fullest XCD
+  const int64_t t16 = nh * ((nqb + kRowsPerWG - 1) / kRowsPerWG);
+  const int64_t partial = t16 % kSlotsPerXcd;
+  int small_rows;
+  if (t16 <= kSlotsPerXcd) {
+    small_rows = nqb;
+  } else if (partial == 0 || partial > kSlotsPerXcd / 2) {
+    small_rows = nqb % kRowsPerWG;
+  } else {
+    const int64_t per_head = (partial * kRowsPerWG + nh - 1) / nh;
+    const int64_t rounded = (per_head + kSmallRows - 1) / kSmallRows * kSmallRows;
+    small_rows = rounded < (int64_t)nqb ? (int)rounded : nqb;
+  }
+  const int nbig = (nqb - small_rows) / kRowsPerWG;
+  const int rest = nqb - nbig * kRowsPerWG;
+  return {nbig, (rest + kSmallRows - 1) / kSmallRows};
+}
+// Workgroups are dealt to the 8 XCDs round-robin by id, so id b runs on XCD b % 8. XCD x takes
+// the heads [x n / 8, (x + 1) n / 8): first all their long tiles, head after head, then all their
+// short ones, so each XCD keeps the pooled keys of the heads it is on
+// (2 * nkb * head_dim * 2 bytes each) in its own L2.
+__host__ __device__ inline int64_t xcd_head_begin(int64_t n_heads, int x) { return n_heads * x / 8; }
+
+inline int64_t select_items_per_xcd(int64_t n_heads, int nqb) {
+  const SelectTiling t = select_tiling(n_heads, nqb);
+  int64_t m = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t nh = xcd_head_begin(n_heads, x + 1) - xcd_head_begin(n_heads, x);
+    m = nh * (t.nbig + t.nsmall) > m ? nh * (t.nbig + t.nsmall) : m;
+  }
+  return m;
+}
+
+// This workgroup's tile: (batch, head) bh and query blocks [row0, row_end). False: no tile.
+__device__ __forceinline__ bool select_work_item(int64_t n_heads, int nqb, int* bh, int* row0,
+                                                 int* row_end) {
+  const int x = (int)(blockIdx.x % 8);
+  const int64_t i = blockIdx.x / 8;
+  const SelectTiling t = select_tiling(n_heads, nqb);
+  const int64_t h0 = xcd_head_begin(n_heads, x);
+  const int64_t nh = xcd_head_begin(n_heads, x + 1) - h0;
+  const int64_t nb = nh * t.nbig;
+  if (i < nb) {
+    *bh = (int)(h0 + i / t.nbig);
+    *row0 = (int)(i % t.nbig) * kRowsPerWG;
+    *row_end = *row0 + kRowsPerWG;
+    return true;
+  }
+  const int64_t j = i - nb;
+  if (j >= nh * t.nsmall) return false;
+  *bh = (int)(h0 + j / t.nsmall);
+  *row0 = t.nbig * kRowsPerWG + (int)(j % t.nsmall) * kSmallRows;
+  *row_end = *row0 + kSmallRows < nqb ? *row0 + kSmallRows : nqb;
+  return true;
 }
 
 template <typename T, int D, int S, int MODE>
@@ -585,23 +643,20 @@ __global__ __launch_bounds__(64 * kWaves) void score_select_kernel(SelectArgs a,
   // and then one 256-bin histogram per wave (phase 2: 8 KiB of 32-bit counts in Top-K mode,
   // 16 KiB of 64-bit masses in mass mode)
   extern __shared__ float s_lds[];
-  const int tiles = (a.nqb + kRowsPerWG - 1) / kRowsPerWG;
-  int64_t item;
-  if (!xcd_work_item((int64_t)n_heads * tiles, &item)) return;
-  const int bh = (int)(item / tiles);
-  const int row0 = (int)(item - (int64_t)bh * tiles) * kRowsPerWG;
+  int bh, row0, row_end;
+  if (!select_work_item(n_heads, a.nqb, &bh, &row0, &row_end)) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
   uint16_t* qlds = reinterpret_cast<uint16_t*>(s_lds + kRowsPerWG * a.lds_stride);
-  pool_q_rows<T, D>(a, qlds, bh, row0, lane, wave);
+  pool_q_rows<T, D>(a, qlds, bh, row0, row_end, lane, wave);
   __syncthreads();
-  score_phase<D>(a, s_lds, qlds, bh, row0, lane, wave);
+  score_phase<D>(a, s_lds, qlds, bh, row0, row_end, lane, wave);
   __syncthreads();
 
   for (int rr = wave; rr < kRowsPerWG; rr += kWaves) {
     const int qi = row0 + rr;
-    if (qi >= a.nqb) break;
+    if (qi >= row_end) break;
     const int64_t row = (int64_t)bh * a.nqb + qi;
     const float* srow = s_lds + rr * a.lds_stride;
     if (MODE == 0)
@@ -766,8 +821,7 @@ hipError_t launch_select_energy(const SelectArgs& a, const float* energy, hipStr
 
 template <typename T, int D, int MODE>
 static hipError_t launch_score_select_dm(const SelectArgs& a, int64_t bh, hipStream_t stream) {
-  const int64_t items = bh * ((a.nqb + kRowsPerWG - 1) / kRowsPerWG);
-  const dim3 grid((unsigned)(8 * ((items + 7) / 8)));
+  const dim3 grid((unsigned)(8 * select_items_per_xcd(bh, a.nqb)));
   const dim3 block(64 * kWaves);
   // the area after the scores holds the pooled queries (8 KiB at most), then one histogram per
   // wave: 256 x 32-bit (Top-K) or 256 x 64-bit (mass)
